@@ -1,0 +1,194 @@
+"""Decode benchmark: one step = reshape_and_cache + paged_attention_decode for every layer.
+
+Default workload: the Llama-3-70B-shaped batch (64 sequences x 4096 tokens, 64 query / 8 kv
+heads, head dim 128, bf16, 80 layers in one 80 GiB K+V pool, 16384 blocks per layer scattered by
+a seeded permutation). Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth, GB/s
+METRIC = "decode KV-read GB/s (% of MI355X HBM peak) + tokens/s per layer-step"
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_452_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def algorithmic_bytes(lens, num_q_heads, num_kv_heads, head_dim, elem=2, block=16):
+    """Bytes one decode launch must move: every cached K and V row of every sequence once per kv
+    head, q in, out back, the used block-table entries and the context lengths."""
+    kv = sum(int(n) for n in lens) * num_kv_heads * head_dim * elem * 2
+    qo = len(lens) * num_q_heads * head_dim * elem * 2
+    tables = sum(-(-int(n) // block) for n in lens) * 4
+    return kv + qo + tables + 4 * len(lens)
+
+
+def source_hash() -> str:
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source and this workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_source_sha256_16") != source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(batch, spec, layers, budget_s=15.0):
+    """The fp64 oracle on the host cores over whole layers of the same batch (bounded)."""
+    import numpy as np
+    import torch
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    t = batch.tables
+    per_layer = algorithmic_bytes(t.context_lens, spec.num_q_heads, spec.num_kv_heads,
+                                  spec.head_dim)
+    done_bytes, cpu_s, d2h_s, n_layers = 0, 0.0, 0.0, 0
+    q = batch.q.cpu()
+    for L in layers:
+        t0 = time.perf_counter()
+        kw = batch.k_pool[L].view(torch.int16).cpu().numpy().view(np.uint16)
+        vw = batch.v_pool[L].view(torch.int16).cpu().numpy().view(np.uint16)
+        d2h_s += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle.paged_decode(q, kw, vw, t.block_tables, t.context_lens, spec.scale,
+                            spec.num_q_heads, spec.num_kv_heads, spec.head_dim, 16, t.num_blocks,
+                            oracle.BF16, threads=threads)
+        cpu_s += time.perf_counter() - t0
+        done_bytes += per_layer
+        n_layers += 1
+        if cpu_s >= budget_s:
+            break
+    return {"value": round(done_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_layers} whole layer(s) of the same batch ({spec.num_seqs} seqs x "
+                      f"{spec.num_q_heads} heads each), fp64, timed from host-resident pools; "
+                      f"device-to-host copy {d2h_s:.2f} s not included",
+            "seconds": round(cpu_s, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this decode path is built and measured on a single "
+              f"MI355X; --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_452_amd as pkv
+    import workloads
+
+    pkv.load_library()
+    dev = "cuda"
+    spec = workloads.SPECS[args.config]
+    t = workloads.make_tables(spec)
+    batch = workloads.make_batch(spec, device=dev, tables=t)
+    S, Hq, Hkv, D, L = (spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                        spec.num_layers)
+    max_ctx = int(t.context_lens.max())
+    pt = args.partition_tokens
+    ws_bytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, max_ctx, pt)
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev) if ws_bytes else None
+    outs = torch.empty((L, S, Hq, D), dtype=batch.q.dtype, device=dev)
+    layers = [(batch.k_pool[i], batch.v_pool[i]) for i in range(L)]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for i, (k, v) in enumerate(layers):
+            pkv.reshape_and_cache(batch.new_key, batch.new_value, k, v, batch.slot_mapping,
+                                  t.num_blocks, 16, stream)
+            if ev is not None:
+                ev[i][0].record(stream)
+            pkv.paged_attention_decode(outs[i], batch.q, k, v, batch.block_tables,
+                                       batch.context_lens, spec.scale, Hq, Hkv, D, 16, max_ctx,
+                                       pt, ws, stream)
+            if ev is not None:
+                ev[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in range(L)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        step(events[k])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    decode_ms = [e[0].elapsed_time(e[1]) for ev in events for e in ev]
+    decode_ms.sort()
+    avg_decode_ms = sum(decode_ms) / len(decode_ms)
+
+    per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D)
+    value = per_launch * L / (ms_step * 1e-3) / 1e9
+    achieved = per_launch / (avg_decode_ms * 1e-3) / 1e9
+    workload = spec.name
+    traffic = measured_traffic(workload)
+    part = pt or pkv.paged_attention_partition_tokens(S, Hq, Hkv, max_ctx, 16)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": workload, "num_seqs": S, "context_lens": "all 4096" if
+                   args.config == 4 else "seeded", "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": 16, "num_layers": L,
+                   "num_blocks_per_layer": t.num_blocks, "partition_tokens": part,
+                   "step": "per layer: reshape_and_cache of the step's new tokens + "
+                           "paged_attention_decode"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s_per_layer_step": round(S * L / (ms_step * 1e-3), 1),
+        "decode_launch_us": {"mean": round(avg_decode_ms * 1e3, 2),
+                             "p10": round(decode_ms[len(decode_ms) // 10] * 1e3, 2),
+                             "p90": round(decode_ms[(9 * len(decode_ms)) // 10] * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": per_launch,
+                     "kernel": "paged_attention_decode (decode kernel + log-sum-exp merge)"},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(batch, spec, range(L))
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,227 @@
+"""PagedAttention decode for AMD Instinct MI355X (gfx950): Python binding of libpagedkv.
+
+Every entry point has the name of the C function it wraps (include/pagedkv.h) and only marshals
+arguments: tensors become device pointers, the current torch stream becomes the hipStream_t,
+a non-OK status becomes a PagedKVError. All computation happens in the HIP library; there is no
+fallback path. The library is loaded from this package directory (libpagedkv.so, built by
+``python -m paged_kv_cache_452_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_BF16 = 0
+PKV_FP16 = 1
+
+EXPORTED = ("kv_pool_bytes", "kv_pool_create", "kv_pool_layer", "kv_pool_destroy",
+            "reshape_and_cache", "paged_attention_partition_tokens",
+            "paged_attention_workspace_bytes", "paged_attention_decode", "pkv_status_string")
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {message} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(build_if_missing: bool = True):
+    """Load libpagedkv.so (building it first only when it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise RuntimeError(f"{LIB_PATH} is not built")
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    lib.kv_pool_bytes.argtypes = [i, i, i, i, i, i]
+    lib.kv_pool_bytes.restype = sz
+    lib.kv_pool_create.argtypes = [ctypes.POINTER(vp), vp, vp, sz, i, i, i, i, i, i]
+    lib.kv_pool_create.restype = i
+    lib.kv_pool_layer.argtypes = [vp, i, ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    lib.kv_pool_layer.restype = i
+    lib.kv_pool_destroy.argtypes = [vp]
+    lib.kv_pool_destroy.restype = None
+    lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.reshape_and_cache.restype = i
+    lib.paged_attention_partition_tokens.argtypes = [i, i, i, i, i]
+    lib.paged_attention_partition_tokens.restype = i
+    lib.paged_attention_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.paged_attention_workspace_bytes.restype = sz
+    lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, i,
+                                           vp, sz, vp]
+    lib.paged_attention_decode.restype = i
+    lib.pkv_status_string.argtypes = [i]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = load_library().pkv_status_string(status).decode()
+        raise PagedKVError(fn, status, msg)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype == torch.float16:
+        return PKV_FP16
+    raise TypeError(f"unsupported element type {t.dtype} (bf16 or fp16)")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _require_cuda(*tensors) -> None:
+    for t in tensors:
+        if t is not None and not isinstance(t, int) and not t.is_cuda:
+            raise ValueError("device tensors required (the library runs on the GPU only)")
+
+
+def pkv_status_string(status: int) -> str:
+    return load_library().pkv_status_string(status).decode()
+
+
+def kv_pool_bytes(num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
+                  block_size: int, dtype: int) -> int:
+    return int(load_library().kv_pool_bytes(num_layers, num_blocks, num_kv_heads, head_dim,
+                                            block_size, dtype))
+
+
+class KVPool:
+    """Host-side geometry of caller-owned K and V pools (kv_pool_create / kv_pool_destroy)."""
+
+    def __init__(self, k_base, v_base, bytes_each: int, num_layers: int, num_blocks: int,
+                 num_kv_heads: int, head_dim: int, block_size: int, dtype: int):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check("kv_pool_create", lib.kv_pool_create(ctypes.byref(h), _ptr(k_base), _ptr(v_base),
+                                                    bytes_each, num_layers, num_blocks,
+                                                    num_kv_heads, head_dim, block_size, dtype))
+        self._h = h
+        self._keep = (k_base, v_base)
+        self.num_layers = num_layers
+
+    def layer(self, layer: int) -> Tuple[int, int]:
+        return kv_pool_layer(self, layer)
+
+    def destroy(self) -> None:
+        if self._h is not None and self._h.value:
+            load_library().kv_pool_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def kv_pool_create(k_base, v_base, bytes_each: int, num_layers: int, num_blocks: int,
+                   num_kv_heads: int, head_dim: int, block_size: int, dtype: int) -> KVPool:
+    return KVPool(k_base, v_base, bytes_each, num_layers, num_blocks, num_kv_heads, head_dim,
+                  block_size, dtype)
+
+
+def kv_pool_layer(pool: KVPool, layer: int) -> Tuple[int, int]:
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    _check("kv_pool_layer", load_library().kv_pool_layer(pool._h, layer, ctypes.byref(k),
+                                                         ctypes.byref(v)))
+    return int(k.value or 0), int(v.value or 0)
+
+
+def kv_pool_destroy(pool: KVPool) -> None:
+    pool.destroy()
+
+
+def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, num_blocks: int,
+                      block_size: int = 16, stream=None) -> None:
+    """Scatter key/value [T][Hkv][D] into the pool slots named by slot_mapping (int64 [T]).
+    k_pool / v_pool: one layer's sub-pool, as a tensor or a device address."""
+    _require_cuda(key, value, k_pool, v_pool, slot_mapping)
+    T, Hkv, D = key.shape
+    _check("reshape_and_cache", load_library().reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping), T, Hkv, D,
+        block_size, num_blocks, _dtype_code(key), _stream(stream)))
+
+
+def paged_attention_partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                     max_context_len: int, block_size: int = 16) -> int:
+    return int(load_library().paged_attention_partition_tokens(
+        num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size))
+
+
+def paged_attention_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                    head_dim: int, block_size: int, max_context_len: int,
+                                    partition_tokens: int = 0) -> int:
+    r = int(load_library().paged_attention_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+        partition_tokens))
+    if r == ctypes.c_size_t(-1).value:
+        raise PagedKVError("paged_attention_workspace_bytes", -1, "PKV_ERR_INVALID_ARG")
+    return r
+
+
+def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale: float,
+                           num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                           max_context_len: int, partition_tokens: int = 0, workspace=None,
+                           stream=None) -> None:
+    """out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s over each sequence's paged K/V."""
+    _require_cuda(out, q, k_pool, v_pool, block_tables, context_lens, workspace)
+    S = q.shape[0]
+    max_blocks = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attention_decode", load_library().paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+        float(scale), num_q_heads, num_kv_heads, head_dim, block_size, S, max_blocks,
+        max_context_len, partition_tokens, _dtype_code(q), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+class Decoder:
+    """Convenience holder of a workspace sized for one decode shape (allocated once)."""
+
+    def __init__(self, num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                 max_context_len: int, block_size: int = 16, partition_tokens: int = 0,
+                 device="cuda"):
+        import torch
+        self.args = (num_q_heads, num_kv_heads, head_dim, block_size)
+        self.max_context_len = max_context_len
+        self.partition_tokens = partition_tokens
+        nbytes = paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 block_size, max_context_len, partition_tokens)
+        self.workspace = (torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=device)
+                          if nbytes > 0 else None)
+
+    def __call__(self, out, q, k_pool, v_pool, block_tables, context_lens, scale, stream=None):
+        Hq, Hkv, D, B = self.args
+        paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, Hq, Hkv,
+                               D, B, self.max_context_len, self.partition_tokens, self.workspace,
+                               stream)

@@ -1,0 +1,97 @@
+"""Shared helpers of the GPU parity tests: run the HIP path, run the oracle, compare."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_452_amd as pkv
+
+MAX_ABS = 1e-2    # attention outputs vs the fp64 oracle (bf16/fp16 in, fp32 accumulation)
+REL_L2 = 2e-3
+
+
+def host_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def say(*args):
+    """Name the case before a GPU step (flushed, so a crash still shows what ran)."""
+    print("[gpu-case]", *args, flush=True)
+    sys.stdout.flush()
+
+
+def words(t: torch.Tensor) -> np.ndarray:
+    """Raw 16-bit words of a (device or host) bf16/fp16 tensor as a host numpy array."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def oracle_dtype(t: torch.Tensor) -> int:
+    return oracle.FP16 if t.dtype == torch.float16 else oracle.BF16
+
+
+def gpu_decode(q, k_layer, v_layer, block_tables, context_lens, scale, Hq, Hkv, max_ctx,
+               partition_tokens=0, out=None):
+    D = q.shape[-1]
+    S = q.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, max_ctx, partition_tokens)
+    ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device) if nbytes else None
+    pkv.paged_attention_decode(out, q, k_layer, v_layer, block_tables, context_lens, scale, Hq,
+                               Hkv, D, 16, max_ctx, partition_tokens, ws)
+    return out
+
+
+def oracle_decode(q, k_layer, v_layer, block_tables, context_lens, scale, Hq, Hkv, num_blocks,
+                  pairs=None, k_words=None, v_words=None):
+    kw = words(k_layer) if k_words is None else k_words
+    vw = words(v_layer) if v_words is None else v_words
+    bt = block_tables.cpu().numpy() if isinstance(block_tables, torch.Tensor) else block_tables
+    cl = context_lens.cpu().numpy() if isinstance(context_lens, torch.Tensor) else context_lens
+    return oracle.paged_decode(words(q), kw, vw, bt, cl, scale, Hq, Hkv, q.shape[-1], 16,
+                               num_blocks, oracle_dtype(q), pairs=pairs, threads=host_threads())
+
+
+def errors(got: torch.Tensor, ref: np.ndarray):
+    g = got.detach().float().cpu().double().numpy().reshape(ref.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    err = g - ref
+    max_abs = float(np.max(np.abs(err))) if err.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(err) / den) if den > 0 else float(np.linalg.norm(err))
+    return max_abs, rel
+
+
+def assert_close(got: torch.Tensor, ref: np.ndarray, what: str = ""):
+    max_abs, rel = errors(got, ref)
+    assert max_abs <= MAX_ABS and rel <= REL_L2, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
+    return max_abs, rel
+
+
+def poison_dead_slots_(k_layer: torch.Tensor, v_layer: torch.Tensor, tables, lens,
+                       num_kv_heads: int, head_dim: int):
+    """Write NaN into the unwritten slots (t >= n) of every sequence's last block, locating
+    them with the oracle's layout function."""
+    idx = []
+    for s, n in enumerate(lens):
+        n = int(n)
+        if n % 16 == 0:
+            continue
+        b = int(tables[s][n // 16])
+        for t in range(n % 16, 16):
+            for h in range(num_kv_heads):
+                for d in range(head_dim):
+                    idx.append((oracle.pool_index(False, b, h, t, d, num_kv_heads, 16, head_dim),
+                                oracle.pool_index(True, b, h, t, d, num_kv_heads, 16, head_dim)))
+    if not idx:
+        return
+    ia = torch.tensor(idx, dtype=torch.long, device=k_layer.device)
+    k_layer.view(-1)[ia[:, 0]] = float("nan")
+    v_layer.view(-1)[ia[:, 1]] = float("nan")

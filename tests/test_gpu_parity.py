@@ -1,0 +1,187 @@
+"""GPU parity: the HIP path against the fp64 oracle on the five decode workloads and edge cases.
+
+Bar: reshape_and_cache and all indexing bit-exact (whole-pool word compare); attention outputs
+within max-abs 1e-2 and relative L2 2e-3 of the oracle.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_452_amd as pkv
+import workloads
+from helpers import (assert_close, gpu_decode, oracle_decode, poison_dead_slots_, say, words)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    yield
+    torch.cuda.synchronize()
+
+
+def _layer(batch, L=0):
+    return batch.k_pool[L], batch.v_pool[L]
+
+
+def _step(batch, layer=0, poison=True):
+    """One decode step on one layer: reshape_and_cache of the new tokens, then decode.
+    Returns (gpu_out, oracle_out, pools bit-exact flag)."""
+    spec, t = batch.spec, batch.tables
+    k, v = _layer(batch, layer)
+    if poison:
+        poison_dead_slots_(k, v, t.block_tables, t.context_lens, spec.num_kv_heads, spec.head_dim)
+    kw, vw = words(k), words(v)
+    # oracle side: host scatter on the host copy
+    oracle.reshape_and_cache(kw, vw, batch.new_key.cpu(), batch.new_value.cpu(), t.slot_mapping,
+                             spec.num_kv_heads, spec.head_dim, 16, t.num_blocks)
+    say("reshape_and_cache", spec.name, "layer", layer)
+    pkv.reshape_and_cache(batch.new_key, batch.new_value, k, v, batch.slot_mapping, t.num_blocks)
+    torch.cuda.synchronize()
+    assert np.array_equal(words(k), kw), "K pool differs after reshape_and_cache"
+    assert np.array_equal(words(v), vw), "V pool differs after reshape_and_cache"
+    say("decode", spec.name, "layer", layer)
+    out = gpu_decode(batch.q, k, v, batch.block_tables, batch.context_lens, spec.scale,
+                     spec.num_q_heads, spec.num_kv_heads, batch.max_context_len)
+    torch.cuda.synchronize()
+    ref = oracle_decode(batch.q, k, v, t.block_tables, t.context_lens, spec.scale,
+                        spec.num_q_heads, spec.num_kv_heads, t.num_blocks, k_words=kw, v_words=vw)
+    return out, ref
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 5])
+def test_decode_step_matches_oracle(idx):
+    spec = workloads.SPECS[idx]
+    batch = workloads.make_batch(spec, device=DEV)
+    out, ref = _step(batch, poison=(idx in (1, 2, 5)))
+    assert_close(out, ref, spec.name)
+
+
+def test_config1_two_steps_cross_block_boundary():
+    spec = workloads.SPECS[1]
+    batch = workloads.make_batch(spec, device=DEV)
+    out, ref = _step(batch)
+    assert_close(out, ref, "step 1")
+    t2 = workloads.append_step(batch.tables)
+    assert t2.context_lens.tolist() == [2, 16, 17, 42]
+    g = torch.Generator(device=DEV).manual_seed(99)
+    b2 = dataclasses.replace(
+        batch, tables=t2,
+        q=workloads.randn(batch.q.shape, batch.q.dtype, g, DEV),
+        new_key=workloads.randn(batch.new_key.shape, batch.q.dtype, g, DEV),
+        new_value=workloads.randn(batch.new_value.shape, batch.q.dtype, g, DEV),
+        block_tables=torch.from_numpy(t2.block_tables).to(DEV),
+        context_lens=torch.from_numpy(t2.context_lens).to(DEV),
+        slot_mapping=torch.from_numpy(t2.slot_mapping).to(DEV))
+    out2, ref2 = _step(b2, poison=False)
+    assert_close(out2, ref2, "step 2")
+
+
+def test_config4_all_80_layers_sampled():
+    """70B-shaped: 80 layers in one 80 GiB pool, decoded layer by layer as the benchmark does;
+    sampled (sequence, head) outputs of sampled layers against the oracle."""
+    spec = workloads.SPECS[4]
+    t = workloads.make_tables(spec)
+    say("config 4: allocating and filling 2 x 40 GiB")
+    batch = workloads.make_batch(spec, device=DEV, tables=t)
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    outs = torch.empty((spec.num_layers, S, Hq, D), dtype=batch.q.dtype, device=DEV)
+    ws_bytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, 4096)
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=DEV)
+    say("config 4: decode 80 layers")
+    for L in range(spec.num_layers):
+        k, v = _layer(batch, L)
+        pkv.paged_attention_decode(outs[L], batch.q, k, v, batch.block_tables, batch.context_lens,
+                                   spec.scale, Hq, Hkv, D, 16, 4096, 0, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    for L in (0, 37, 79):
+        pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, S, 48), rng.integers(0, Hq, 48))]
+        k, v = _layer(batch, L)
+        ref = oracle_decode(batch.q, k, v, t.block_tables, t.context_lens, spec.scale, Hq, Hkv,
+                            t.num_blocks, pairs=pairs)
+        got = torch.stack([outs[L, s, h] for s, h in pairs])
+        assert_close(got, ref, f"layer {L}")
+    del batch, outs
+    torch.cuda.empty_cache()
+
+
+def _random_case(Hq, Hkv, D, lens, dtype=torch.bfloat16, seed=0, extra_blocks=7):
+    """A small paged batch with NaN-poisoned unused blocks and dead slots."""
+    lens = np.asarray(lens, np.int32)
+    spec = workloads.Spec(0, f"case Hq={Hq} Hkv={Hkv} D={D} lens={lens.tolist()}", len(lens), Hq,
+                          Hkv, D, "bf16" if dtype == torch.bfloat16 else "fp16", 1, seed=seed)
+    need = sum(-(-int(n) // 16) for n in lens)
+    t = workloads.make_tables(spec, lens=lens, num_blocks=max(need + extra_blocks, 1), seed=seed)
+    b = workloads.make_batch(spec, device=DEV, tables=t)
+    k, v = _layer(b)
+    poison_dead_slots_(k, v, t.block_tables, t.context_lens, Hkv, D)
+    return spec, t, b
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,lens", [
+    (8, 8, 128, torch.bfloat16, [1, 2, 15, 16, 17, 31, 32, 33]),       # MHA, ragged tails
+    (32, 8, 128, torch.float16, [100, 257, 1000]),                      # GQA fp16
+    (12, 4, 64, torch.bfloat16, [5, 64, 65, 300]),                      # group of 3, d64
+    (64, 2, 128, torch.bfloat16, [40, 513]),                            # group of 32: 2 head tiles
+    (16, 1, 64, torch.float16, [2049]),                                 # MQA, many blocks
+    (4, 4, 64, torch.bfloat16, [0, 3, 0, 16]),                          # empty sequences
+])
+def test_edge_shapes(Hq, Hkv, D, dtype, lens):
+    spec, t, b = _random_case(Hq, Hkv, D, lens, dtype, seed=len(lens) * 7 + Hq)
+    k, v = _layer(b)
+    say("edge", spec.name)
+    out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, Hq, Hkv,
+                     max(int(max(lens)), 1))
+    torch.cuda.synchronize()
+    ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, Hq, Hkv,
+                        t.num_blocks)
+    assert_close(out, ref, spec.name)
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(out[s]).item() == 0
+
+
+@pytest.mark.parametrize("partition_tokens", [16, 32, 256, 512, 4096, 0])
+def test_partition_sizes_agree_with_oracle(partition_tokens):
+    spec, t, b = _random_case(32, 8, 128, [1, 255, 256, 257, 1500, 4000], seed=11)
+    k, v = _layer(b)
+    say("partition", partition_tokens)
+    out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, 4000,
+                     partition_tokens)
+    torch.cuda.synchronize()
+    ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 32, 8,
+                        t.num_blocks)
+    assert_close(out, ref, f"partition {partition_tokens}")
+
+
+def test_long_sequence_many_partitions():
+    spec, t, b = _random_case(32, 8, 128, [32768, 100], seed=12)
+    k, v = _layer(b)
+    for pt in (256, 0):
+        say("long sequence, partition", pt)
+        out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, 32768, pt)
+        torch.cuda.synchronize()
+        ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 32, 8,
+                            t.num_blocks)
+        assert_close(out, ref, f"32k partition {pt}")
+
+
+def test_max_context_fills_block_table():
+    lens = [64 * 16, 64 * 16 - 1]
+    spec, t, b = _random_case(8, 2, 128, lens, seed=13)
+    assert t.block_tables.shape[1] == 64
+    k, v = _layer(b)
+    out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 8, 2, 64 * 16)
+    torch.cuda.synchronize()
+    ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 8, 2,
+                        t.num_blocks)
+    assert_close(out, ref, "max context")
