@@ -85,6 +85,20 @@ def cpu_baseline(batch, spec, layers, budget_s=15.0):
             "seconds": round(cpu_s, 3)}
 
 
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3) -> int:
+    """A plain device copy of known size, to scale the HBM byte counters of a profiler run."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "reps": reps}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +107,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this decode path is built and measured on a single "
@@ -103,6 +119,8 @@ def main() -> int:
     import paged_kv_cache_452_amd as pkv
     import workloads
 
+    if args.calibrate_copy:
+        return calibrate_copy()
     pkv.load_library()
     dev = "cuda"
     spec = workloads.SPECS[args.config]
