@@ -138,19 +138,22 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* k_pool, v
                              hipStream_t stream);
 
 /*
- * The partition length (tokens, a multiple of block_size) paged_attention_decode uses when it is
- * passed partition_tokens == 0. Sequences longer than one partition are split over several
- * workgroups and joined by a log-sum-exp merge, so that few long sequences still fill the GPU.
- * Returns 0 on invalid arguments.
+ * The partition size (tokens, a multiple of block_size) paged_attention_decode uses when it is
+ * passed partition_tokens == 0. A partition is the part of one sequence that one workgroup
+ * reads; a sequence of nb blocks is split into ceil(nb / (partition_tokens / block_size))
+ * partitions of near-equal length, joined by a log-sum-exp merge, so that a few long sequences
+ * still fill the GPU. At most 4096 tokens (256 blocks). Returns 0 on invalid arguments.
  */
 int paged_attention_partition_tokens(int num_seqs, int num_q_heads, int num_kv_heads,
                                      int max_context_len, int block_size);
 
 /*
  * Workspace bytes paged_attention_decode needs for these arguments (fp32 partial results:
- * num_seqs * num_q_heads * P * (head_dim + 2) * 4 with P = ceil(max_context_len /
- * partition length)). 0 when every sequence fits one partition (no workspace needed).
- * partition_tokens: 0 = the library's choice, else a positive multiple of block_size.
+ * num_seqs * num_q_heads * P * (head_dim + 2) * 4 with P = ceil(ceil(max_context_len /
+ * block_size) / (partition size / block_size))). 0 when every sequence fits one partition (no
+ * workspace needed).
+ * partition_tokens: 0 = the library's choice, else a positive multiple of block_size; values
+ * above 4096 act as 4096.
  * Returns (size_t)-1 on invalid arguments.
  */
 size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
@@ -174,7 +177,8 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  *   block_tables device int32 [num_seqs][max_blocks_per_seq].
  *   context_lens device int32 [num_seqs], each in [0, min(max_context_len, max_blocks_per_seq*B)].
  *   scale        multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
- *   partition_tokens 0 = library choice, else a positive multiple of block_size.
+ *   partition_tokens 0 = library choice, else a positive multiple of block_size (most tokens one
+ *                workgroup reads; values above 4096 act as 4096).
  *   workspace    device, >= paged_attention_workspace_bytes(...) bytes, 16-byte aligned; may be
  *                NULL when that size is 0. Contents on entry are ignored and left undefined.
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_ALIGNMENT, PKV_ERR_WORKSPACE,

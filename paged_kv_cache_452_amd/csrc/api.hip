@@ -56,30 +56,31 @@ int device_cus() {
   return v;
 }
 
-// Partition length in blocks. With enough (sequence, kv head, head tile) wavefronts to give
-// every compute unit about eight, a sequence is never split (single pass, no merge). Otherwise
-// the longest power-of-two partition of at least 16 blocks (256 tokens) that still reaches that
-// count on the longest allowed sequence wins, so that few long sequences spread over the whole
-// GPU while the merge traffic stays small.
+// Partition size (blocks per decode workgroup, at most kMaxPartBlocks = 256). A workgroup's four
+// wavefronts split its partition and combine in LDS; sequences longer than one partition are
+// split into near-equal partitions joined by the merge kernel. The longest power-of-two
+// partition that still gives every compute unit about two workgroups (eight wavefronts) on the
+// longest allowed sequence wins: few long sequences then spread over the whole GPU, while large
+// batches keep whole sequences in one workgroup and need no merge at all.
 int choose_part_blocks(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len) {
   const int nb_max = (max_context_len + pkv::kBlock - 1) / pkv::kBlock;
   if (nb_max <= 16) return nb_max > 0 ? nb_max : 1;
   const int group = num_q_heads / num_kv_heads;
   const long tiles = (long)num_seqs * num_kv_heads *
                      ((group + pkv::kMaxGroupTile - 1) / pkv::kMaxGroupTile);
-  const long target = 8L * device_cus();
-  if (tiles >= target) return nb_max;
-  int best = 16;
-  for (int pb = 32; pb < nb_max; pb *= 2) {
-    if (tiles * ((nb_max + pb - 1) / pb) >= target) best = pb;
-    else break;
+  const long target = 2L * device_cus();
+  for (int pb = pkv::kMaxPartBlocks; pb > 16; pb /= 2) {
+    if (tiles * ((nb_max + pb - 1) / pb) >= target) return pb < nb_max ? pb : nb_max;
   }
-  return best;
+  return 16;
 }
 
 int resolve_part_blocks(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len,
                         int partition_tokens) {
-  if (partition_tokens > 0) return partition_tokens / pkv::kBlock;
+  if (partition_tokens > 0) {
+    const int pb = partition_tokens / pkv::kBlock;
+    return pb < pkv::kMaxPartBlocks ? pb : pkv::kMaxPartBlocks;
+  }
   return choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, max_context_len);
 }
 
@@ -181,8 +182,8 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
   if (block_size != pkv::kBlock) return (size_t)-1;
   const int pb = resolve_part_blocks(num_seqs, num_q_heads, num_kv_heads, max_context_len,
                                      partition_tokens);
-  const long part_tok = (long)pb * block_size;
-  const long max_parts = max_context_len > 0 ? (max_context_len + part_tok - 1) / part_tok : 1;
+  const long nb_max = ((long)max_context_len + block_size - 1) / block_size;
+  const long max_parts = nb_max > 0 ? (nb_max + pb - 1) / pb : 1;
   if (max_parts <= 1) return 0;
   size_t r = 0;
   if (!mul_ok((size_t)num_seqs * (size_t)num_q_heads, (size_t)max_parts, &r)) return (size_t)-1;
@@ -211,8 +212,8 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
 
   const int pb = resolve_part_blocks(num_seqs, num_q_heads, num_kv_heads, max_context_len,
                                      partition_tokens);
-  const long part_tok = (long)pb * block_size;
-  const long max_parts = max_context_len > 0 ? (max_context_len + part_tok - 1) / part_tok : 1;
+  const long nb_max = ((long)max_context_len + block_size - 1) / block_size;
+  const long max_parts = nb_max > 0 ? (nb_max + pb - 1) / pb : 1;
   if (max_parts > 65535) return PKV_ERR_UNSUPPORTED;
   const size_t need = paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
                                                       head_dim, block_size, max_context_len,

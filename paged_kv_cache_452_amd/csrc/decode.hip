@@ -41,6 +41,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // A score may exceed the reference maximum by this much (log2 units) before the reference moves.
 constexpr float kLazyRescale = 8.0f;
 
+// Tile buffers per wavefront (blocks in flight = kRing - 1), sized to stay within 256 VGPRs so
+// two wavefronts fit on each SIMD.
+template <int D>
+constexpr int kRing = D == 128 ? 4 : 8;
+
+
 template <bool BF16>
 struct Elem;
 
@@ -97,15 +103,37 @@ struct Elem<false> {
 
 __device__ __forceinline__ u32x4 load16(const char* p) { return *(const u32x4*)p; }
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeLaunch a) {
+// K/V tiles are streamed: each is read once per launch, so the loads carry the non-temporal
+// hint (measured on MI355X: random 4 KiB tile reads reach ~6.8 TB/s this way, ~6.05 TB/s with
+// default-policy loads).
+__device__ __forceinline__ u32x4 load16_stream(const char* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+// Blocks of a partition [first, first + count) are split evenly over the partitions of a
+// sequence: partition p of np covers blocks [p*nb/np, (p+1)*nb/np). Shared with the merge.
+__device__ __forceinline__ int partitions_of(int n, int part_blocks, int max_parts) {
+  const int nb = (n + kBlock - 1) / kBlock;
+  // (clamped so that a context length above the promised maximum stays inside the workspace)
+  return n > 0 ? min((nb + part_blocks - 1) / part_blocks, max_parts) : 1;
+}
+
+template <int D, bool BF16, int RING>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void
+paged_decode_kernel(DecodeLaunch a) {
   using E = Elem<BF16>;
   constexpr int NQ = D / 32;   // 16-byte K loads (and QK matrix ops) per block
   constexpr int NV = D / 32;   // 16-byte V loads per block
   constexpr int NO = D / 16;   // 16-column output chunks
   constexpr size_t kTileBytes = (size_t)kBlock * D * 2;
+  constexpr int kRow = D + 4;  // LDS row stride (floats) of the combine buffer
 
-  const int lane = threadIdx.x;
+  __shared__ float sm_o[kWaves][kMaxGroupTile][kRow];
+  __shared__ float sm_m[kWaves][kMaxGroupTile];
+  __shared__ float sm_l[kWaves][kMaxGroupTile];
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int hl = lane & 15;    // query head within the tile (operand column)
   const int kg = lane >> 4;    // lane quarter: dims 8kg.. of each 32-dim chunk / tokens 4kg..
 
@@ -117,15 +145,22 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeLaunch a) {
   const int part = blockIdx.y;
 
   const int n = a.context_lens[s];
-  const int part_tok = a.part_blocks * kBlock;
-  // (clamped so that a context length above the promised maximum stays inside the workspace)
-  const int nparts = min(n > 0 ? (n + part_tok - 1) / part_tok : 1, a.max_parts);
-  if (part >= nparts) return;
-  const int tok0 = part * part_tok;
-  const int tok1 = min(n, tok0 + part_tok);
-  const int nblk = (tok1 - tok0 + kBlock - 1) / kBlock;
+  const int nparts = partitions_of(n, a.part_blocks, a.max_parts);
+  if (part >= nparts) return;  // uniform over the workgroup
+  const int nb_seq = (n + kBlock - 1) / kBlock;
+  const int pb0 = (int)((long)part * nb_seq / nparts);        // partition's first block
+  const int pb1 = (int)((long)(part + 1) * nb_seq / nparts);  // one past its last
+  const int npb = pb1 - pb0;
+  const int wb0 = pb0 + wave * npb / kWaves;                   // this wave's blocks
+  const int nblk = pb0 + (wave + 1) * npb / kWaves - wb0;     // <= 64
+  const int tok0 = wb0 * kBlock;
+  const int tok1 = min(n, tok0 + nblk * kBlock);
   const int h0 = g * a.group + ht * kMaxGroupTile;
   const int nvalid = min(kMaxGroupTile, a.group - ht * kMaxGroupTile);
+
+  // Block ids of this wave's blocks: lane i holds logical block wb0 + i.
+  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks + wb0;
+  const int bids = lane < nblk ? trow[lane] : 0;
 
   // Q^T operand: lane (hl, kg) holds q[h0 + hl][32c + 8kg .. +8] for each 32-dim chunk c.
   u32x4 qv[NQ];
@@ -137,11 +172,6 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeLaunch a) {
     }
   }
 
-  // Block ids of the partition, 64 per VGPR (lane i holds logical block chunk_base + i).
-  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks + (size_t)part * a.part_blocks;
-  int chunk_base = 0;
-  int bids = lane < nblk ? trow[lane] : 0;
-
   const size_t blk_stride = (size_t)a.num_kv_heads * kTileBytes;
   const char* kbase = (const char*)a.k_pool + (size_t)g * kTileBytes + lane * 16;
   const char* vbase = (const char*)a.v_pool + (size_t)g * kTileBytes + lane * 16;
@@ -152,33 +182,19 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeLaunch a) {
 #pragma unroll
   for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 kc[NQ], vc[NV], kn[NQ], vn[NV];
-  if (nblk > 0) {
-    const int b = __builtin_amdgcn_readfirstlane(bids);
+  // Ring of RING tile buffers: block j + RING - 1 is loading while block j is computed.
+  u32x4 kr[RING][NQ], vr[RING][NV];
+  auto issue = [&](int j, u32x4* kd, u32x4* vd) {
+    const int b = __builtin_amdgcn_readlane(bids, j);
     const char* kp = kbase + (size_t)b * blk_stride;
     const char* vp = vbase + (size_t)b * blk_stride;
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) kc[c] = load16(kp + c * 1024);
+    for (int c = 0; c < NQ; ++c) kd[c] = load16_stream(kp + c * 1024);
 #pragma unroll
-    for (int c = 0; c < NV; ++c) vc[c] = load16(vp + c * 1024);
-  }
+    for (int c = 0; c < NV; ++c) vd[c] = load16_stream(vp + c * 1024);
+  };
 
-  for (int j = 0; j < nblk; ++j) {
-    // Prefetch block j + 1 while block j is computed.
-    if (j + 1 < nblk) {
-      if (j + 1 - chunk_base == 64) {
-        chunk_base += 64;
-        bids = chunk_base + lane < nblk ? trow[chunk_base + lane] : 0;
-      }
-      const int b = __builtin_amdgcn_readlane(bids, j + 1 - chunk_base);
-      const char* kp = kbase + (size_t)b * blk_stride;
-      const char* vp = vbase + (size_t)b * blk_stride;
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) kn[c] = load16(kp + c * 1024);
-#pragma unroll
-      for (int c = 0; c < NV; ++c) vn[c] = load16(vp + c * 1024);
-    }
-
+  auto process = [&](const u32x4* kc, u32x4* vc, int j) {
     // Scores: lane holds S[token 4kg + e][head hl], e = 0..3.
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -233,44 +249,93 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeLaunch a) {
       o[i] = E::pv(phi, vv, o[i]);
       o[i] = E::pv(plo, vv, o[i]);
     }
+  };
 
+  // Prologue: blocks 0 .. RING-2 in flight.
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) kc[c] = kn[c];
+  for (int u = 0; u < RING - 1; ++u) {
+    if (u < nblk) issue(u, kr[u], vr[u]);
+  }
+  // Steady state: every iteration issues one block and computes one, with no conditions, so
+  // the compiler can count outstanding loads exactly.
+  const int steady = nblk >= RING - 1 ? (nblk - (RING - 1)) / RING * RING : 0;
+  for (int j0 = 0; j0 < steady; j0 += RING) {
 #pragma unroll
-    for (int c = 0; c < NV; ++c) vc[c] = vn[c];
+    for (int u = 0; u < RING; ++u) {
+      issue(j0 + u + RING - 1, kr[(u + RING - 1) % RING], vr[(u + RING - 1) % RING]);
+      process(kr[u], vr[u], j0 + u);
+    }
+  }
+  // Tail: at most 2*RING - 2 blocks; block steady + u sits in slot u % RING.
+#pragma unroll
+  for (int u = 0; u < 2 * RING - 2; ++u) {
+    const int j = steady + u;
+    if (j < nblk) {
+      if (j + RING - 1 < nblk) {
+        issue(j + RING - 1, kr[(u + RING - 1) % RING], vr[(u + RING - 1) % RING]);
+      }
+      process(kr[u % RING], vr[u % RING], j);
+    }
   }
 
   // Row sums of head hl over the four lane quarters.
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
 
+  // Combine the workgroup's waves: O_wg = sum_w 2^(m_w - M) O_w, L = sum_w 2^(m_w - M) l_w.
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int i = 0; i < NO; ++i) sm_o[wave][4 * kg + e][16 * i + hl] = o[i][e];
+  }
+  if (kg == 0) {
+    sm_m[wave][hl] = m_run;
+    sm_l[wave][hl] = l_tot;
+  }
+  __syncthreads();
+
+  constexpr int kHeadsPerWave = kMaxGroupTile / kWaves;   // 4
+  constexpr int kLanesPerHead = 64 / kHeadsPerWave;       // 16
+  constexpr int kDims = D / kLanesPerHead;                // 8 (d128) or 4 (d64)
+  const int head = wave * kHeadsPerWave + lane / kLanesPerHead;
+  const int d0 = (lane % kLanesPerHead) * kDims;
+  if (head >= nvalid) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][head]);
+  float L = 0.f;
+  float acc[kDims];
+#pragma unroll
+  for (int i = 0; i < kDims; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = sm_m[w][head];
+    const float c = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);  // empty wave -> 0
+    L += c * sm_l[w][head];
+#pragma unroll
+    for (int i = 0; i < kDims; ++i) acc[i] += c * sm_o[w][head][d0 + i];
+  }
+  const size_t row = (size_t)s * a.num_q_heads + h0 + head;
   if (nparts == 1) {
-    unsigned short* out = (unsigned short*)a.out;
+    const float inv = L > 0.f ? 1.f / L : 0.f;   // n == 0 -> zeros
+    unsigned short r[kDims];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int head = 4 * kg + e;
-      const float L = __shfl(l_tot, head);
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      if (head < nvalid) {
-        unsigned short* orow = out + ((size_t)s * a.num_q_heads + h0 + head) * D;
-#pragma unroll
-        for (int i = 0; i < NO; ++i) orow[16 * i + hl] = E::store(o[i][e] * inv);
-      }
+    for (int i = 0; i < kDims; ++i) r[i] = E::store(acc[i] * inv);
+    unsigned short* dst = (unsigned short*)a.out + row * D + d0;
+    if constexpr (kDims == 8) {
+      *(u32x4*)dst = u32x4{r[0] | (unsigned)r[1] << 16, r[2] | (unsigned)r[3] << 16,
+                           r[4] | (unsigned)r[5] << 16, r[6] | (unsigned)r[7] << 16};
+    } else {
+      *(u32x2*)dst = u32x2{r[0] | (unsigned)r[1] << 16, r[2] | (unsigned)r[3] << 16};
     }
   } else {
+    float* w = a.ws_o + (row * a.max_parts + part) * D + d0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int head = 4 * kg + e;
-      if (head < nvalid) {
-        float* w = a.ws_o + (((size_t)s * a.num_q_heads + h0 + head) * a.max_parts + part) * D;
-#pragma unroll
-        for (int i = 0; i < NO; ++i) w[16 * i + hl] = o[i][e];
-      }
-    }
-    if (kg == 0 && hl < nvalid) {
-      float* ml = a.ws_ml + (((size_t)s * a.num_q_heads + h0 + hl) * a.max_parts + part) * 2;
-      ml[0] = m_run;
-      ml[1] = l_tot;
+    for (int i = 0; i < kDims; ++i) w[i] = acc[i];
+    if (lane % kLanesPerHead == 0) {
+      float* ml = a.ws_ml + (row * a.max_parts + part) * 2;
+      ml[0] = M;
+      ml[1] = L;
     }
   }
 }
@@ -296,8 +361,7 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch a) {
   const int s = blockIdx.x / a.num_q_heads;
   const int h = blockIdx.x % a.num_q_heads;
   const int n = a.context_lens[s];
-  const int part_tok = a.part_blocks * kBlock;
-  const int nparts = min(n > 0 ? (n + part_tok - 1) / part_tok : 1, a.max_parts);
+  const int nparts = partitions_of(n, a.part_blocks, a.max_parts);
   if (nparts <= 1) return;
   const size_t base = ((size_t)s * a.num_q_heads + h) * a.max_parts;
   const float* ml = a.ws_ml + base * 2;
@@ -327,7 +391,8 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch a) {
 template <int D, bool BF16>
 hipError_t launch_typed(const DecodeLaunch& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads * a.head_tiles), (unsigned)a.max_parts);
-  hipLaunchKernelGGL((paged_decode_kernel<D, BF16>), grid, dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((paged_decode_kernel<D, BF16, kRing<D>>), grid, dim3(64 * kWaves), 0, stream,
+                     a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.max_parts <= 1) return err;
   hipLaunchKernelGGL((merge_kernel<D, BF16>), dim3((unsigned)(a.num_seqs * a.num_q_heads)),

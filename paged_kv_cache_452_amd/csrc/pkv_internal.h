@@ -9,6 +9,9 @@ namespace pkv {
 
 constexpr int kBlock = 16;          // tokens per physical block this build supports
 constexpr int kMaxGroupTile = 16;   // query heads per wave (matrix-core N dimension)
+constexpr int kWaves = 4;           // wavefronts per decode workgroup
+constexpr int kWaveBlocks = 64;     // blocks one wavefront handles at most (ids in one VGPR)
+constexpr int kMaxPartBlocks = kWaves * kWaveBlocks;  // blocks per workgroup (partition)
 
 struct DecodeLaunch {
   void* out;
@@ -26,7 +29,8 @@ struct DecodeLaunch {
   int group;            // num_q_heads / num_kv_heads
   int head_tiles;       // ceil(group / 16)
   int max_blocks;       // block table row length
-  int part_blocks;      // blocks per partition
+  int part_blocks;      // most blocks of one partition (<= kMaxPartBlocks); a sequence of nb
+                        // blocks has ceil(nb / part_blocks) partitions of near-equal length
   int max_parts;        // partitions of the longest allowed sequence
 };
 
