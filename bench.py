@@ -106,7 +106,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--workgroups", type=int, default=0,
+                    help="decode workgroups (0: the library's choice)")
     ap.add_argument("--layers", type=int, default=0,
                     help="layers in the pool (default: the workload's own; more layers of fresh "
                          "data keep a small single-layer workload from being served out of the "
@@ -136,9 +137,9 @@ def main() -> int:
     S, Hq, Hkv, D, L = (spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                         spec.num_layers)
     max_ctx = int(t.context_lens.max())
-    pt = args.partition_tokens
-    ws_bytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, max_ctx, pt)
-    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev) if ws_bytes else None
+    nwg = args.workgroups
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, max_ctx, nwg),
+                           dev)
     outs = torch.empty((L, S, Hq, D), dtype=batch.q.dtype, device=dev)
     layers = [(batch.k_pool[i], batch.v_pool[i]) for i in range(L)]
     stream = torch.cuda.current_stream()
@@ -149,13 +150,13 @@ def main() -> int:
                                   t.num_blocks, 16, stream)
             pkv.paged_attention_decode(outs[i], batch.q, k, v, batch.block_tables,
                                        batch.context_lens, spec.scale, Hq, Hkv, D, 16, max_ctx,
-                                       pt, ws, stream)
+                                       nwg, ws, stream)
 
     def sweep_decode():
         for i, (k, v) in enumerate(layers):
             pkv.paged_attention_decode(outs[i], batch.q, k, v, batch.block_tables,
                                        batch.context_lens, spec.scale, Hq, Hkv, D, 16, max_ctx,
-                                       pt, ws, stream)
+                                       nwg, ws, stream)
 
     def timed(fn, reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -170,20 +171,20 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # Timed region A: whole steps (per layer: reshape_and_cache, then decode), no markers inside.
-    ms_total = timed(step, args.steps)
-    ms_step = ms_total / args.steps
     # Timed region B: the decode kernel alone, launched back to back over the layers; the mean
     # launch duration is the region's time over the launch count.
     reps_b = max(1, args.steps // 2)
     avg_decode_ms = timed(sweep_decode, reps_b) / (reps_b * L)
+    # Timed region A: whole steps (per layer: reshape_and_cache, then decode), no markers inside.
+    ms_total = timed(step, args.steps)
+    ms_step = ms_total / args.steps
 
     per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D)
     value = per_launch * L / (ms_step * 1e-3) / 1e9
     achieved = per_launch / (avg_decode_ms * 1e-3) / 1e9
     workload = spec.name
     traffic = measured_traffic(workload)
-    part = pt or pkv.paged_attention_partition_tokens(S, Hq, Hkv, max_ctx, 16)
+    grid = nwg or pkv.paged_attention_num_workgroups(S, Hq, Hkv, max_ctx, 16)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -200,20 +201,21 @@ def main() -> int:
         "config": {"workload": workload if args.layers <= 0 else f"{workload}, {L} layers", "num_seqs": S, "context_lens": "all 4096" if
                    args.config == 4 else "seeded", "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": 16, "num_layers": L,
-                   "num_blocks_per_layer": t.num_blocks, "partition_tokens": part,
+                   "num_blocks_per_layer": t.num_blocks, "decode_workgroups": grid,
                    "step": "per layer: reshape_and_cache of the step's new tokens + "
                            "paged_attention_decode"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_per_layer_step": round(S * L / (ms_step * 1e-3), 1),
         "decode_launch_us": round(avg_decode_ms * 1e3, 2),
-        "timing": "value: K whole steps between two HIP events on the launch stream; "
-                  "roofline.achieved: back-to-back decode launches over all layers between two "
-                  "HIP events (mean launch duration)",
+        "timing": "roofline.achieved: back-to-back decode launches over all layers between two "
+                  "HIP events on the launch stream (mean launch duration), timed first; value: K "
+                  "whole steps between two HIP events",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": per_launch,
-                     "kernel": "paged_attention_decode (decode kernel + log-sum-exp merge)"},
+                     "kernel": "paged_attention_decode (one persistent decode kernel; split "
+                               "streams merged in it)"},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(batch, spec, range(L))

@@ -138,27 +138,25 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* k_pool, v
                              hipStream_t stream);
 
 /*
- * The partition size (tokens, a multiple of block_size) paged_attention_decode uses when it is
- * passed partition_tokens == 0. A partition is the part of one sequence that one workgroup
- * reads; a sequence of nb blocks is split into ceil(nb / (partition_tokens / block_size))
- * partitions of near-equal length, joined by a log-sum-exp merge, so that a few long sequences
- * still fill the GPU. At most 4096 tokens (256 blocks). Returns 0 on invalid arguments.
+ * Workgroups paged_attention_decode launches when it is passed num_workgroups == 0: enough to fill
+ * every compute unit of the current device, fewer for small batches. The decode lays every
+ * (sequence, kv head) stream of blocks end to end and gives each workgroup an equal contiguous
+ * share, so long and skewed sequences are spread evenly; a stream cut between workgroups is
+ * joined by a log-sum-exp merge of fp32 partial results. Returns 0 on invalid arguments.
  */
-int paged_attention_partition_tokens(int num_seqs, int num_q_heads, int num_kv_heads,
-                                     int max_context_len, int block_size);
+int paged_attention_num_workgroups(int num_seqs, int num_q_heads, int num_kv_heads,
+                                   int max_context_len, int block_size);
 
 /*
- * Workspace bytes paged_attention_decode needs for these arguments (fp32 partial results:
- * num_seqs * num_q_heads * P * (head_dim + 2) * 4 with P = ceil(ceil(max_context_len /
- * block_size) / (partition size / block_size))). 0 when every sequence fits one partition (no
- * workspace needed).
- * partition_tokens: 0 = the library's choice, else a positive multiple of block_size; values
- * above 4096 act as 4096.
+ * Workspace bytes paged_attention_decode needs for these arguments: with G workgroups
+ * (num_workgroups, or the library's choice when it is 0),
+ *     bytes = G * 2 * 16 * (head_dim + 2) * 4 + roundup(4 G, 256)
+ * (fp32 partials of at most two split streams per workgroup, then G arrival counters).
  * Returns (size_t)-1 on invalid arguments.
  */
 size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                        int head_dim, int block_size, int max_context_len,
-                                       int partition_tokens);
+                                       int num_workgroups);
 
 /*
  * Decode attention over a paged KV cache. For each sequence s, query head h, kv head
@@ -177,10 +175,14 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  *   block_tables device int32 [num_seqs][max_blocks_per_seq].
  *   context_lens device int32 [num_seqs], each in [0, min(max_context_len, max_blocks_per_seq*B)].
  *   scale        multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
- *   partition_tokens 0 = library choice, else a positive multiple of block_size (most tokens one
- *                workgroup reads; values above 4096 act as 4096).
- *   workspace    device, >= paged_attention_workspace_bytes(...) bytes, 16-byte aligned; may be
- *                NULL when that size is 0. Contents on entry are ignored and left undefined.
+ *   num_workgroups 0 = library choice (paged_attention_num_workgroups), else the number of
+ *                workgroups (1 .. 2^20); results depend on it only through rounding order.
+ *   workspace    device, >= paged_attention_workspace_bytes(...) bytes, 256-byte aligned. Its
+ *                last 4 G bytes are arrival counters and the rest is scratch. Zero-fill the whole
+ *                buffer once before its first use; every call that completes leaves its counters
+ *                zero again, so the buffer can serve any later call it is large enough for.
+ *                Calls that may run concurrently need separate workspaces.
+ * At most 2048 sequences per call (PKV_ERR_UNSUPPORTED above).
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_ALIGNMENT, PKV_ERR_WORKSPACE,
  * PKV_ERR_HIP. Deterministic: identical inputs give bit-identical outputs (no atomics).
  */
@@ -188,7 +190,7 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
                                   const int32_t* block_tables, const int32_t* context_lens,
                                   float scale, int num_q_heads, int num_kv_heads, int head_dim,
                                   int block_size, int num_seqs, int max_blocks_per_seq,
-                                  int max_context_len, int partition_tokens, pkv_dtype dtype,
+                                  int max_context_len, int num_workgroups, pkv_dtype dtype,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */

@@ -19,7 +19,7 @@ PKV_BF16 = 0
 PKV_FP16 = 1
 
 EXPORTED = ("kv_pool_bytes", "kv_pool_create", "kv_pool_layer", "kv_pool_destroy",
-            "reshape_and_cache", "paged_attention_partition_tokens",
+            "reshape_and_cache", "paged_attention_num_workgroups",
             "paged_attention_workspace_bytes", "paged_attention_decode", "pkv_status_string")
 
 
@@ -54,8 +54,8 @@ def load_library(build_if_missing: bool = True):
     lib.kv_pool_destroy.restype = None
     lib.reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
     lib.reshape_and_cache.restype = i
-    lib.paged_attention_partition_tokens.argtypes = [i, i, i, i, i]
-    lib.paged_attention_partition_tokens.restype = i
+    lib.paged_attention_num_workgroups.argtypes = [i, i, i, i, i]
+    lib.paged_attention_num_workgroups.restype = i
     lib.paged_attention_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.paged_attention_workspace_bytes.restype = sz
     lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, i,
@@ -172,26 +172,35 @@ def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, num_blocks: int,
         block_size, num_blocks, _dtype_code(key), _stream(stream)))
 
 
-def paged_attention_partition_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int,
-                                     max_context_len: int, block_size: int = 16) -> int:
-    return int(load_library().paged_attention_partition_tokens(
+def paged_attention_num_workgroups(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                   max_context_len: int, block_size: int = 16) -> int:
+    return int(load_library().paged_attention_num_workgroups(
         num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size))
 
 
 def paged_attention_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                                     head_dim: int, block_size: int, max_context_len: int,
-                                    partition_tokens: int = 0) -> int:
+                                    num_workgroups: int = 0) -> int:
     r = int(load_library().paged_attention_workspace_bytes(
         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
-        partition_tokens))
+        num_workgroups))
     if r == ctypes.c_size_t(-1).value:
         raise PagedKVError("paged_attention_workspace_bytes", -1, "PKV_ERR_INVALID_ARG")
     return r
 
 
+def new_workspace(num_bytes: int, device="cuda"):
+    """A decode workspace of at least num_bytes, zero-filled (its counters must start at zero;
+    every completed call leaves them zero). None when no workspace is needed."""
+    import torch
+    if num_bytes <= 0:
+        return None
+    return torch.zeros((num_bytes + 3) // 4, dtype=torch.int32, device=device)
+
+
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale: float,
                            num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
-                           max_context_len: int, partition_tokens: int = 0, workspace=None,
+                           max_context_len: int, num_workgroups: int = 0, workspace=None,
                            stream=None) -> None:
     """out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s over each sequence's paged K/V."""
     _require_cuda(out, q, k_pool, v_pool, block_tables, context_lens, workspace)
@@ -201,27 +210,26 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
     _check("paged_attention_decode", load_library().paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
         float(scale), num_q_heads, num_kv_heads, head_dim, block_size, S, max_blocks,
-        max_context_len, partition_tokens, _dtype_code(q), _ptr(workspace), ws_bytes,
+        max_context_len, num_workgroups, _dtype_code(q), _ptr(workspace), ws_bytes,
         _stream(stream)))
 
 
 class Decoder:
-    """Convenience holder of a workspace sized for one decode shape (allocated once)."""
+    """Convenience holder of a zero-initialised workspace sized for one decode shape (allocated
+    once, reused by every call on one stream)."""
 
     def __init__(self, num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                 max_context_len: int, block_size: int = 16, partition_tokens: int = 0,
+                 max_context_len: int, block_size: int = 16, num_workgroups: int = 0,
                  device="cuda"):
-        import torch
         self.args = (num_q_heads, num_kv_heads, head_dim, block_size)
         self.max_context_len = max_context_len
-        self.partition_tokens = partition_tokens
+        self.num_workgroups = num_workgroups
         nbytes = paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                 block_size, max_context_len, partition_tokens)
-        self.workspace = (torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=device)
-                          if nbytes > 0 else None)
+                                                 block_size, max_context_len, num_workgroups)
+        self.workspace = new_workspace(nbytes, device)
 
     def __call__(self, out, q, k_pool, v_pool, block_tables, context_lens, scale, stream=None):
         Hq, Hkv, D, B = self.args
         paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, scale, Hq, Hkv,
-                               D, B, self.max_context_len, self.partition_tokens, self.workspace,
+                               D, B, self.max_context_len, self.num_workgroups, self.workspace,
                                stream)

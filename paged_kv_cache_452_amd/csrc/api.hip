@@ -1,4 +1,4 @@
-// C ABI of libpagedkv: argument checks, pool geometry, partition choice, kernel launches.
+// C ABI of libpagedkv: argument checks, pool geometry, grid choice, kernel launches.
 // The declarations and their contracts are in include/pagedkv.h.
 
 #include "pagedkv.h"
@@ -56,42 +56,49 @@ int device_cus() {
   return v;
 }
 
-// Partition size (blocks per decode workgroup, at most kMaxPartBlocks = 256). A workgroup's four
-// wavefronts split its partition and combine in LDS; sequences longer than one partition are
-// split into near-equal partitions joined by the merge kernel. The longest power-of-two
-// partition that still gives every compute unit about two workgroups (eight wavefronts) on the
-// longest allowed sequence wins: few long sequences then spread over the whole GPU, while large
-// batches keep whole sequences in one workgroup and need no merge at all.
-int choose_part_blocks(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len) {
-  const int nb_max = (max_context_len + pkv::kBlock - 1) / pkv::kBlock;
-  if (nb_max <= 16) return nb_max > 0 ? nb_max : 1;
+// Workgroups of a decode launch when the caller leaves the choice to the library: enough to
+// fill every compute unit (kWorkgroupsPerCU resident each), but no more than one per 64 block
+// positions of the largest possible batch (16 per wavefront), so that small batches are not cut
+// into slivers. The kernel spreads the actual positions evenly over the wavefronts it is given.
+int default_workgroups(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len) {
   const int group = num_q_heads / num_kv_heads;
-  const long tiles = (long)num_seqs * num_kv_heads *
-                     ((group + pkv::kMaxGroupTile - 1) / pkv::kMaxGroupTile);
-  const long target = 2L * device_cus();
-  for (int pb = pkv::kMaxPartBlocks; pb > 16; pb /= 2) {
-    if (tiles * ((nb_max + pb - 1) / pb) >= target) return pb < nb_max ? pb : nb_max;
-  }
-  return 16;
+  const long streams = (long)num_seqs * num_kv_heads *
+                       ((group + pkv::kMaxGroupTile - 1) / pkv::kMaxGroupTile);
+  const long nb_max = ((long)max_context_len + pkv::kBlock - 1) / pkv::kBlock;
+  const long positions = streams * nb_max;
+  const long full = (long)pkv::kWorkgroupsPerCU * device_cus();
+  long g = (positions + 63) / 64;  // >= 16 blocks per wavefront
+  if (g > full) g = full;
+  return g > 0 ? (int)g : 1;
 }
 
-int resolve_part_blocks(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len,
-                        int partition_tokens) {
-  if (partition_tokens > 0) {
-    const int pb = partition_tokens / pkv::kBlock;
-    return pb < pkv::kMaxPartBlocks ? pb : pkv::kMaxPartBlocks;
-  }
-  return choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, max_context_len);
-}
+constexpr int kMaxWorkgroups = 1 << 20;
 
 bool decode_shape_ok(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len,
-                     int block_size, int partition_tokens) {
+                     int block_size, int num_workgroups) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return false;
   if (num_q_heads % num_kv_heads != 0) return false;
   if (block_size <= 0) return false;
-  if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % block_size != 0))
-    return false;
+  if (num_workgroups < 0 || num_workgroups > kMaxWorkgroups) return false;
   return true;
+}
+
+int resolve_workgroups(int num_seqs, int num_q_heads, int num_kv_heads, int max_context_len,
+                       int num_workgroups) {
+  return num_workgroups > 0
+             ? num_workgroups
+             : default_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len);
+}
+
+// Workspace for `grid` workgroups (one range each): (m, l) and partial outputs from the start,
+// arrival counters in the last 4 bytes per workgroup of the caller's buffer. Keeping the
+// counters at the end means calls with fewer workgroups never write partials over the counters of
+// calls with more, so one zero-filled buffer serves any sequence of calls it is large enough for.
+size_t counter_bytes(int grid) { return ((size_t)grid * sizeof(unsigned) + 255) & ~(size_t)255; }
+size_t ml_bytes(int grid) { return (size_t)grid * 2 * pkv::kMaxGroupTile * 2 * sizeof(float); }
+size_t workspace_bytes_for(int grid, int head_dim) {
+  return counter_bytes(grid) + ml_bytes(grid) +
+         (size_t)grid * 2 * pkv::kMaxGroupTile * head_dim * sizeof(float);
 }
 
 }  // namespace
@@ -164,63 +171,57 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* k_pool, v
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-int paged_attention_partition_tokens(int num_seqs, int num_q_heads, int num_kv_heads,
-                                     int max_context_len, int block_size) {
+int paged_attention_num_workgroups(int num_seqs, int num_q_heads, int num_kv_heads,
+                                   int max_context_len, int block_size) {
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size, 0) ||
       block_size != pkv::kBlock)
     return 0;
-  return choose_part_blocks(num_seqs, num_q_heads, num_kv_heads, max_context_len) * block_size;
+  return default_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len);
 }
 
 size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                        int head_dim, int block_size, int max_context_len,
-                                       int partition_tokens) {
+                                       int num_workgroups) {
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size,
-                       partition_tokens) ||
-      head_dim <= 0)
+                       num_workgroups) ||
+      head_dim <= 0 || block_size != pkv::kBlock)
     return (size_t)-1;
-  if (block_size != pkv::kBlock) return (size_t)-1;
-  const int pb = resolve_part_blocks(num_seqs, num_q_heads, num_kv_heads, max_context_len,
-                                     partition_tokens);
-  const long nb_max = ((long)max_context_len + block_size - 1) / block_size;
-  const long max_parts = nb_max > 0 ? (nb_max + pb - 1) / pb : 1;
-  if (max_parts <= 1) return 0;
-  size_t r = 0;
-  if (!mul_ok((size_t)num_seqs * (size_t)num_q_heads, (size_t)max_parts, &r)) return (size_t)-1;
-  if (!mul_ok(r, (size_t)(head_dim + 2) * sizeof(float), &r)) return (size_t)-1;
-  return r;
+  const int grid = resolve_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                                      num_workgroups);
+  return workspace_bytes_for(grid, head_dim);
 }
 
 pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_tables, const int32_t* context_lens,
                                   float scale, int num_q_heads, int num_kv_heads, int head_dim,
                                   int block_size, int num_seqs, int max_blocks_per_seq,
-                                  int max_context_len, int partition_tokens, pkv_dtype dtype,
+                                  int max_context_len, int num_workgroups, pkv_dtype dtype,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size,
-                       partition_tokens) ||
+                       num_workgroups) ||
       max_blocks_per_seq < 0 || !isfinite(scale))
     return PKV_ERR_INVALID_ARG;
   if (!supported_shape(head_dim, block_size, dtype)) return PKV_ERR_UNSUPPORTED;
   if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
+  if (num_seqs > pkv::kMaxSeqs) return PKV_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  const int head_tiles = (group + pkv::kMaxGroupTile - 1) / pkv::kMaxGroupTile;
+  // Flattened block positions and token counts are 32-bit on the device.
+  if (max_blocks_per_seq > 2147483647 / block_size) return PKV_ERR_UNSUPPORTED;
+  if ((long double)num_seqs * max_blocks_per_seq * num_kv_heads * head_tiles >= 2147483647.0L)
+    return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
     return PKV_ERR_ALIGNMENT;
 
-  const int pb = resolve_part_blocks(num_seqs, num_q_heads, num_kv_heads, max_context_len,
-                                     partition_tokens);
-  const long nb_max = ((long)max_context_len + block_size - 1) / block_size;
-  const long max_parts = nb_max > 0 ? (nb_max + pb - 1) / pb : 1;
-  if (max_parts > 65535) return PKV_ERR_UNSUPPORTED;
-  const size_t need = paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
-                                                      head_dim, block_size, max_context_len,
-                                                      partition_tokens);
-  if (need == (size_t)-1) return PKV_ERR_INVALID_ARG;
+  const int grid = resolve_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                                      num_workgroups);
+  const size_t need = workspace_bytes_for(grid, head_dim);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(workspace)) return PKV_ERR_ALIGNMENT;
+  if (need > 0 && ((uintptr_t)workspace & 255u)) return PKV_ERR_ALIGNMENT;
 
   pkv::DecodeLaunch a;
   a.out = out;
@@ -229,19 +230,21 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
   a.v_pool = v_pool;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  const size_t o_elems = (size_t)num_seqs * num_q_heads * (size_t)max_parts * head_dim;
-  a.ws_o = need > 0 ? (float*)workspace : nullptr;
-  a.ws_ml = need > 0 ? (float*)workspace + o_elems : nullptr;
+  char* ws = (char*)workspace;
+  a.ws_ml = need > 0 ? (float*)ws : nullptr;
+  a.ws_o = need > 0 ? (float*)(ws + ml_bytes(grid)) : nullptr;
+  a.counters = need > 0 ? (unsigned*)(ws + (workspace_bytes & ~(size_t)3) -
+                                      (size_t)grid * sizeof(unsigned))
+                        : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
-  a.group = num_q_heads / num_kv_heads;
-  a.head_tiles = (a.group + pkv::kMaxGroupTile - 1) / pkv::kMaxGroupTile;
+  a.group = group;
+  a.head_tiles = head_tiles;
   a.max_blocks = max_blocks_per_seq;
-  a.part_blocks = pb;
-  a.max_parts = (int)max_parts;
-  const hipError_t err = pkv::launch_decode(a, head_dim, dtype == PKV_BF16, stream);
+  a.max_tokens = max_blocks_per_seq * block_size;
+  const hipError_t err = pkv::launch_decode(a, grid, head_dim, dtype == PKV_BF16, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

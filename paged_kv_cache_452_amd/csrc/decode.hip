@@ -1,27 +1,42 @@
-// Paged-attention decode kernels for gfx950 (MI355X).
+// Paged-attention decode kernel for gfx950 (MI355X).
 //
-// One wavefront (64 lanes) owns one (sequence, kv head, group tile of <= 16 query heads,
-// context partition). It walks the partition's logical blocks through the block table
-// ("PagedAttention and KV Cache Management" (blog.sejan.dev), section "Under the Hood: The
-// PagedAttention CUDA Kernel": physical_block_id = block_table[seq_id, logical_block_id]) and,
-// per 16-token block:
+// Work decomposition. Every (sequence s, kv head g, tile of <= 16 query heads) is one *stream* of
+// nb_s = ceil(n_s / 16) blocks. The streams are laid end to end, sequence-major, into one
+// flattened space of W = sum_s nb_s * (kv heads * head tiles) block positions, and the launch's
+// workgroups cut that space into equal contiguous ranges. A workgroup therefore reads the same
+// number of blocks (to within one) whatever the mix of context lengths: a 32k-token sequence is
+// spread over many workgroups and a batch of short ones is packed into few, with no per-sequence
+// partition size to tune and no tail of idle compute units. Each workgroup derives the plan itself
+// from context_lens (a prefix sum in LDS), so the host needs no device data.
+//
+// Inside a range the four wavefronts interleave block by block (wave i takes positions
+// r0 + i, r0 + i + 4, ...), so all four always work on the same stream. Per 16-token block a
+// wavefront follows the block table ("PagedAttention and KV Cache Management"
+// (blog.sejan.dev), section "Under the Hood: The PagedAttention CUDA Kernel":
+// physical_block_id = block_table[seq_id, logical_block_id]) and:
 //   * reads the K tile and the V tile straight from the pool: 64 lanes x 16 bytes per load
 //     instruction, each instruction one contiguous 1 KiB range; the pool's tile order makes
 //     every lane's 16 bytes a ready matrix-core operand, so nothing is staged or shuffled;
 //   * scores S[token][head] = K_tile[16 x D] . Q^T[D x 16] with D/32 v_mfma_f32_16x16x32
-//     (bf16 or f16) — all query heads of a GQA group share the one K read;
+//     (bf16 or f16) -- all query heads of a GQA group share the one K read;
 //   * keeps an online softmax with a lazily moved reference maximum: the reference m only moves
 //     (and the running sum and output get rescaled) when a score exceeds it by more than 2^8,
 //     so probabilities stay <= 256 and the common path needs no cross-lane traffic;
 //   * accumulates O[head][dim] += P[head][token] . V_tile[token][dim] with v_mfma_f32_16x16x16,
 //     P split into a 16-bit high part and a 16-bit residual so the product keeps fp32-level
-//     precision of P;
-// then either writes the normalised output (sequence fits one partition) or the partition's
-// unnormalised (m, l, O) for the log-sum-exp merge kernel.
+//     precision of P.
+// Tiles are prefetched RING-1 blocks ahead through a ring of registers that runs across stream
+// boundaries, and nothing else is read from memory on the common path: block ids come from a
+// register window of 64 per wavefront, and the q rows of the range's first streams are copied
+// into LDS at the start. When a stream ends, the four wavefronts combine their (m, l, O) in LDS.
+// A stream that lies wholly inside the range is normalised and stored. A stream cut by a range
+// boundary leaves an fp32 partial (m, l, O) in the workspace; the last of its workgroups to finish
+// (an agent-scope counter, reset by that workgroup) merges all of them in range order, so the
+// result does not depend on which workgroup came last.
 //
-// Softmax identity used by the merge: with per-partition reference m_p, l_p = sum exp(x - m_p)
+// Softmax identity used by both combines: with per-part reference m_p, l_p = sum exp(x - m_p)
 // and O_p = sum exp(x - m_p) v, the full result is
-//   sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p   for any M (here M = max_p m_p),
+//   sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p   for any M >= max_p m_p,
 // scores being kept in log2 units (x * scale * log2 e).
 
 #include "pkv_internal.h"
@@ -41,11 +56,15 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // A score may exceed the reference maximum by this much (log2 units) before the reference moves.
 constexpr float kLazyRescale = 8.0f;
 
+// q rows (query heads) a workgroup stages in LDS for the first streams of its range.
+constexpr int kQRows = 64;
+// Parts whose loads one merge round issues together.
+constexpr int kMergeRound = 8;
+
 // Tile buffers per wavefront (blocks in flight = kRing - 1), sized to stay within 256 VGPRs so
-// two wavefronts fit on each SIMD.
+// two workgroups fit on each compute unit. 64 (the tile-id window) is a multiple of both.
 template <int D>
 constexpr int kRing = D == 128 ? 4 : 8;
-
 
 template <bool BF16>
 struct Elem;
@@ -104,18 +123,27 @@ struct Elem<false> {
 __device__ __forceinline__ u32x4 load16(const char* p) { return *(const u32x4*)p; }
 
 // K/V tiles are streamed: each is read once per launch, so the loads carry the non-temporal
-// hint (measured on MI355X: random 4 KiB tile reads reach ~6.8 TB/s this way, ~6.05 TB/s with
+// hint (measured on MI355X: random 4 KiB tile reads reach ~7.0 TB/s this way, ~6.2 TB/s with
 // default-policy loads).
 __device__ __forceinline__ u32x4 load16_stream(const char* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
 
-// Blocks of a partition [first, first + count) are split evenly over the partitions of a
-// sequence: partition p of np covers blocks [p*nb/np, (p+1)*nb/np). Shared with the merge.
-__device__ __forceinline__ int partitions_of(int n, int part_blocks, int max_parts) {
-  const int nb = (n + kBlock - 1) / kBlock;
-  // (clamped so that a context length above the promised maximum stays inside the workspace)
-  return n > 0 ? min((nb + part_blocks - 1) / part_blocks, max_parts) : 1;
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// s_waitcnt vmcnt(0): every vector memory access of this wave has completed. The rare loads of
+// the main loop (the next stream's q, the next window of tile ids) are followed by this wait so
+// that, where the paths join, only the ring's tile loads are outstanding and the compiler keeps
+// the exact, deep waits of the common path.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup ranges: workgroup w of nwg covers flattened positions [start(w), start(w + 1)).
+__device__ __forceinline__ int range_start(int w, int nwg, int W) {
+  return (int)((long)w * W / nwg);
+}
+// The workgroup whose range holds position p (0 <= p < W): the last w with start(w) <= p.
+__device__ __forceinline__ int range_owner(int p, int nwg, int W) {
+  return (int)(((long)(p + 1) * nwg - 1) / W);
 }
 
 template <int D, bool BF16, int RING>
@@ -127,54 +155,207 @@ paged_decode_kernel(DecodeLaunch a) {
   constexpr int NO = D / 16;   // 16-column output chunks
   constexpr size_t kTileBytes = (size_t)kBlock * D * 2;
   constexpr int kRow = D + 4;  // LDS row stride (floats) of the combine buffer
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kHeadsPerWave = kMaxGroupTile / kWaves;   // 4 heads per wave in the combine
+  constexpr int kLanesPerHead = 64 / kHeadsPerWave;       // 16
+  constexpr int kDims = D / kLanesPerHead;                // 8 (d128) or 4 (d64)
+  constexpr int kChunks = D / 8;                          // 16-byte chunks per q row
+  constexpr int kQLoads = kQRows * kChunks / kThreads;
+  static_assert(64 % RING == 0, "tile-id windows must hold whole ring turns");
 
+  __shared__ int s_ps[kMaxSeqs + 1];  // s_ps[s] = blocks of sequences 0..s-1
+  __shared__ int s_len[kMaxSeqs];     // context lengths (clamped to the table row)
+  __shared__ int s_scan[kThreads];    // scan partials; later the staged q rows' sources
   __shared__ float sm_o[kWaves][kMaxGroupTile][kRow];
   __shared__ float sm_m[kWaves][kMaxGroupTile];
   __shared__ float sm_l[kWaves][kMaxGroupTile];
+  __shared__ u32x4 s_q[kQRows][kChunks];  // staged q rows of the range's first streams
+  __shared__ int s_last[2];
 
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
+  const int lane = tid & 63;
   const int hl = lane & 15;    // query head within the tile (operand column)
   const int kg = lane >> 4;    // lane quarter: dims 8kg.. of each 32-dim chunk / tokens 4kg..
+  const int S = a.num_seqs;
 
-  int idx = blockIdx.x;
-  const int ht = idx % a.head_tiles;
-  idx /= a.head_tiles;
-  const int g = idx % a.num_kv_heads;
-  const int s = idx / a.num_kv_heads;
-  const int part = blockIdx.y;
-
-  const int n = a.context_lens[s];
-  const int nparts = partitions_of(n, a.part_blocks, a.max_parts);
-  if (part >= nparts) return;  // uniform over the workgroup
-  const int nb_seq = (n + kBlock - 1) / kBlock;
-  const int pb0 = (int)((long)part * nb_seq / nparts);        // partition's first block
-  const int pb1 = (int)((long)(part + 1) * nb_seq / nparts);  // one past its last
-  const int npb = pb1 - pb0;
-  const int wb0 = pb0 + wave * npb / kWaves;                   // this wave's blocks
-  const int nblk = pb0 + (wave + 1) * npb / kWaves - wb0;     // <= 64
-  const int tok0 = wb0 * kBlock;
-  const int tok1 = min(n, tok0 + nblk * kBlock);
-  const int h0 = g * a.group + ht * kMaxGroupTile;
-  const int nvalid = min(kMaxGroupTile, a.group - ht * kMaxGroupTile);
-
-  // Block ids of this wave's blocks: lane i holds logical block wb0 + i.
-  const int32_t* trow = a.block_tables + (size_t)s * a.max_blocks + wb0;
-  const int bids = lane < nblk ? trow[lane] : 0;
-
-  // Q^T operand: lane (hl, kg) holds q[h0 + hl][32c + 8kg .. +8] for each 32-dim chunk c.
-  u32x4 qv[NQ];
+  // ---- Plan: block counts per sequence and their prefix sum, in LDS. ----
   {
-    const char* qrow = (const char*)a.q + ((size_t)s * a.num_q_heads + h0 + hl) * D * 2;
-#pragma unroll
-    for (int c = 0; c < NQ; ++c) {
-      qv[c] = hl < nvalid ? load16(qrow + (32 * c + 8 * kg) * 2) : u32x4{0u, 0u, 0u, 0u};
+    const int chunk = (S + kThreads - 1) / kThreads;
+    const int lo = min(S, tid * chunk);
+    const int hi = min(S, lo + chunk);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) {
+      const int n = min(max(a.context_lens[i], 0), a.max_tokens);
+      s_len[i] = n;
+      sum += (n + kBlock - 1) / kBlock;
+    }
+    s_scan[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    int base = s_scan[tid] - sum;
+    for (int i = lo; i < hi; ++i) {
+      s_ps[i] = base;
+      base += (s_len[i] + kBlock - 1) / kBlock;
+    }
+    if (tid == kThreads - 1) s_ps[S] = s_scan[kThreads - 1];
+    __syncthreads();
+  }
+
+  // Empty sequences (n == 0) own no positions; their output is zero.
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    if (s_len[s] == 0) {
+      u32x4* dst = (u32x4*)((unsigned short*)a.out + (size_t)s * a.num_q_heads * D);
+      for (int c = tid; c < a.num_q_heads * D / 8; c += kThreads) dst[c] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
-  const size_t blk_stride = (size_t)a.num_kv_heads * kTileBytes;
-  const char* kbase = (const char*)a.k_pool + (size_t)g * kTileBytes + lane * 16;
-  const char* vbase = (const char*)a.v_pool + (size_t)g * kTileBytes + lane * 16;
+  const int Hh = a.num_kv_heads * a.head_tiles;  // streams per sequence
+  const int W = uniform(Hh * s_ps[S]);
+  const int nwg = min((int)gridDim.x, W);
+  const int wg = blockIdx.x;
+  if (wg >= nwg) return;  // uniform over the workgroup
+  const int r0 = range_start(wg, nwg, W);
+  const int r1 = range_start(wg + 1, nwg, W);
+
+  // Sequence whose streams hold flattened position p: the last s with Hh * s_ps[s] <= p.
+  auto seq_of = [&](int p) {
+    const int x = p / Hh;
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_ps[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+
+  // ---- Streams (uniform cursor). ----
+  struct Stream {
+    int s, gh;        // sequence, kv head * head tiles + head tile
+    int start, end;   // flattened positions [start, end)
+    int n;            // context length
+    int h0, nvalid;   // first query head of the tile, valid heads in it
+  };
+  auto stream_at = [&](int s, int gh) {
+    Stream t;
+    t.s = s;
+    t.gh = gh;
+    if (s < S) {
+      const int pb = uniform(s_ps[s]);
+      const int nb = uniform(s_ps[s + 1]) - pb;
+      t.n = uniform(s_len[s]);
+      t.start = Hh * pb + gh * nb;
+      t.end = t.start + nb;
+      const int g = gh / a.head_tiles;
+      const int ht = gh - g * a.head_tiles;
+      t.h0 = g * a.group + ht * kMaxGroupTile;
+      t.nvalid = min(kMaxGroupTile, a.group - ht * kMaxGroupTile);
+    } else {  // past the last stream
+      t.n = 0;
+      t.start = t.end = W;
+      t.h0 = 0;
+      t.nvalid = 0;
+    }
+    return t;
+  };
+  auto stream_after = [&](const Stream& c) {
+    int gh = c.gh + 1, s = c.s;
+    if (gh == Hh) {
+      gh = 0;
+      ++s;
+      while (s < S && uniform(s_ps[s + 1]) == uniform(s_ps[s])) ++s;  // skip empty sequences
+    }
+    return stream_at(s, gh);
+  };
+
+  Stream cur;
+  {
+    const int s0 = uniform(seq_of(r0));
+    const int pb = uniform(s_ps[s0]);
+    const int nb = uniform(s_ps[s0 + 1]) - pb;
+    cur = stream_at(s0, (r0 - Hh * pb) / nb);
+  }
+
+  // ---- q: the head rows of the range's first streams, staged in LDS for all four waves. ----
+  int staged_left;  // staged streams after the current one
+  int next_qrow;    // LDS row of the next staged stream
+  {
+    int rows = 0, nstaged = 0;
+    Stream t = cur;
+    while (t.start < r1 && rows + t.nvalid <= kQRows) {
+      if (tid >= rows && tid < rows + t.nvalid)
+        s_scan[tid] = t.s * a.num_q_heads + t.h0 + (tid - rows);  // source row of staged row
+      rows += t.nvalid;
+      ++nstaged;
+      t = stream_after(t);
+    }
+    __syncthreads();
+    u32x4 buf[kQLoads];
+#pragma unroll
+    for (int u = 0; u < kQLoads; ++u) {
+      const int c = tid + kThreads * u;
+      const int row = c / kChunks;
+      buf[u] = row < rows
+                   ? load16((const char*)a.q + ((size_t)s_scan[row] * D + (c % kChunks) * 8) * 2)
+                   : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kQLoads; ++u) {
+      const int c = tid + kThreads * u;
+      if (c / kChunks < rows) s_q[c / kChunks][c % kChunks] = buf[u];
+    }
+    staged_left = nstaged - 1;
+    next_qrow = cur.nvalid;
+  }
+
+  // ---- Tile ids: lane l of window c holds the tile of this wave's position 64c + l. ----
+  const int span = r1 - r0;
+  const int mw = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;  // this wave's blocks
+  auto window = [&](int c) -> unsigned {
+    const int p = r0 + wave + kWaves * (64 * c + lane);
+    if (p >= r1) return 0u;
+    const int s = seq_of(p);
+    const int pb = s_ps[s];
+    const int nb = s_ps[s + 1] - pb;
+    const int r = p - Hh * pb;
+    const int gh = r / nb;
+    const int j = r - gh * nb;
+    const int g = gh / a.head_tiles;
+    return (unsigned)a.block_tables[(size_t)s * a.max_blocks + j] * (unsigned)a.num_kv_heads +
+           (unsigned)g;
+  };
+  unsigned win_a = window(0);
+  unsigned win_b = mw > 64 ? window(1) : 0u;
+  wait_vmem();
+  __syncthreads();  // staged q visible to every wave
+  int chunk_a = 0;
+  auto tile_of = [&](int m) -> unsigned {
+    const unsigned w = (m >> 6) == chunk_a ? win_a : win_b;
+    return __builtin_amdgcn_readlane(w, m & 63);
+  };
+
+  // Q^T operand: lane (hl, kg) holds q[h0 + hl][32c + 8kg .. +8] for each 32-dim chunk c.
+  u32x4 qv[NQ];
+  auto q_from_lds = [&](int row0, int nvalid) {
+#pragma unroll
+    for (int c = 0; c < NQ; ++c)
+      qv[c] = hl < nvalid ? s_q[row0 + hl][4 * c + kg] : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto q_from_memory = [&](const Stream& t) {
+    const char* qrow = (const char*)a.q + ((size_t)t.s * a.num_q_heads + t.h0 + hl) * D * 2;
+#pragma unroll
+    for (int c = 0; c < NQ; ++c)
+      qv[c] = hl < t.nvalid ? load16(qrow + (32 * c + 8 * kg) * 2) : u32x4{0u, 0u, 0u, 0u};
+  };
+  q_from_lds(0, cur.nvalid);
+
+  const char* kbase = (const char*)a.k_pool + lane * 16;
+  const char* vbase = (const char*)a.v_pool + lane * 16;
 
   float m_run = -INFINITY;  // reference maximum of head hl (log2 units)
   float l_run = 0.f;        // sum of p over this lane's tokens for head hl
@@ -182,28 +363,201 @@ paged_decode_kernel(DecodeLaunch a) {
 #pragma unroll
   for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Ring of RING tile buffers: block j + RING - 1 is loading while block j is computed.
+  // Combine layout: 16 lanes per head, kDims consecutive dims per lane.
+  const int head = wave * kHeadsPerWave + lane / kLanesPerHead;
+  const int d0 = (lane % kLanesPerHead) * kDims;
+
+  // Normalise and store kDims consecutive dims of output row `row`.
+  auto store_out = [&](size_t row, const float* acc, float L) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    unsigned short r[kDims];
+#pragma unroll
+    for (int i = 0; i < kDims; ++i) r[i] = E::store(acc[i] * inv);
+    unsigned short* dst = (unsigned short*)a.out + row * D + d0;
+    if constexpr (kDims == 8) {
+      *(u32x4*)dst = u32x4{r[0] | (unsigned)r[1] << 16, r[2] | (unsigned)r[3] << 16,
+                           r[4] | (unsigned)r[5] << 16, r[6] | (unsigned)r[7] << 16};
+    } else {
+      *(u32x2*)dst = u32x2{r[0] | (unsigned)r[1] << 16, r[2] | (unsigned)r[3] << 16};
+    }
+  };
+
+  // Split streams of this range: 0 = the one holding r0, 1 = the one holding r1 - 1.
+  Stream split0, split1;
+  bool has0 = false, has1 = false;
+
+  // ---- End of a stream: combine the four waves, then store it or leave its partial. ----
+  auto finish_stream = [&]() {
+    // The next stream's q: from LDS when staged (no memory access), else from memory, waited for
+    // at once so that only ring loads stay outstanding on the common path.
+    const Stream nxt = stream_after(cur);
+    if (nxt.start < r1) {
+      if (staged_left > 0) {
+        q_from_lds(next_qrow, nxt.nvalid);
+        next_qrow += nxt.nvalid;
+        --staged_left;
+      } else {
+        q_from_memory(nxt);
+        wait_vmem();
+      }
+    }
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+      for (int i = 0; i < NO; ++i) sm_o[wave][4 * kg + e][16 * i + hl] = o[i][e];
+    }
+    if (kg == 0) {
+      sm_m[wave][hl] = m_run;
+      sm_l[wave][hl] = l_tot;
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int i = 0; i < NO; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+
+    const bool complete = cur.start >= r0 && cur.end <= r1;  // uniform
+    const int slot = cur.start <= r0 ? 0 : 1;
+    if (head < cur.nvalid) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][head]);
+      float L = 0.f;
+      float acc[kDims];
+#pragma unroll
+      for (int i = 0; i < kDims; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw_ = sm_m[w][head];
+        const float c = mw_ == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw_ - M);  // idle wave
+        L += c * sm_l[w][head];
+#pragma unroll
+        for (int i = 0; i < kDims; ++i) acc[i] += c * sm_o[w][head][d0 + i];
+      }
+      if (complete) {
+        store_out((size_t)cur.s * a.num_q_heads + cur.h0 + head, acc, L);
+      } else {
+        // Written through to the device's coherence point (agent-scope stores): the merging
+        // workgroup may run on another XCD, behind another L2.
+        const size_t pidx = ((size_t)wg * 2 + slot) * kMaxGroupTile + head;
+        float* po = a.ws_o + pidx * D + d0;
+#pragma unroll
+        for (int i = 0; i < kDims; ++i)
+          __hip_atomic_store(po + i, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane % kLanesPerHead == 0) {
+          __hip_atomic_store(a.ws_ml + pidx * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a.ws_ml + pidx * 2 + 1, L, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    if (!complete) {
+      if (slot == 0) {
+        split0 = cur;
+        has0 = true;
+      } else {
+        split1 = cur;
+        has1 = true;
+      }
+    }
+    __syncthreads();  // the combine buffer is free again
+    cur = nxt;
+  };
+
+  // ---- Merge of a split stream by the last of its workgroups to finish. ----
+  // Rounds of kMergeRound parts: each lane issues the (m, l) and its output slice of every part
+  // of the round before using any of them (one memory round trip per round), then folds the round
+  // into a running maximum. Loads are agent-scope: the partials were written through from other
+  // XCDs.
+  auto merge_stream = [&](const Stream& st) {
+    if (head >= st.nvalid) return;  // uniform over each 16-lane head group
+    const int wa = range_owner(st.start, nwg, W);
+    const int np = range_owner(st.end - 1, nwg, W) - wa + 1;
+    const int slot_a = range_start(wa, nwg, W) == st.start ? 0 : 1;
+    auto part_idx = [&](int k) {  // partial index of part k (workgroup wa + k)
+      return ((size_t)(wa + k) * 2 + (k == 0 ? slot_a : 0)) * kMaxGroupTile + head;
+    };
+    auto ld = [](const float* p) {
+      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    float M = -INFINITY, L = 0.f;
+    float acc[kDims];
+#pragma unroll
+    for (int i = 0; i < kDims; ++i) acc[i] = 0.f;
+    for (int k0 = 0; k0 < np; k0 += kMergeRound) {  // parts in a fixed order
+      float mp[kMergeRound], lp[kMergeRound];
+      unsigned long long ov[kMergeRound][kDims / 2];
+#pragma unroll
+      for (int u = 0; u < kMergeRound; ++u) {
+        const size_t pi = part_idx(min(k0 + u, np - 1));  // past the end: reread, weight 0
+        mp[u] = ld(a.ws_ml + pi * 2);
+        lp[u] = ld(a.ws_ml + pi * 2 + 1);
+        const unsigned long long* po = (const unsigned long long*)(a.ws_o + pi * D + d0);
+#pragma unroll
+        for (int i = 0; i < kDims / 2; ++i)
+          ov[u][i] = __hip_atomic_load(po + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float Mr = M;
+#pragma unroll
+      for (int u = 0; u < kMergeRound; ++u) {
+        if (k0 + u < np) Mr = fmaxf(Mr, mp[u]);
+      }
+      const float rescale = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mr);
+      L *= rescale;
+#pragma unroll
+      for (int i = 0; i < kDims; ++i) acc[i] *= rescale;
+#pragma unroll
+      for (int u = 0; u < kMergeRound; ++u) {
+        const float c = (k0 + u < np && mp[u] != -INFINITY) ? __builtin_amdgcn_exp2f(mp[u] - Mr)
+                                                             : 0.f;
+        L += c * lp[u];
+#pragma unroll
+        for (int i = 0; i < kDims / 2; ++i) {
+          acc[2 * i] += c * __uint_as_float((unsigned)ov[u][i]);
+          acc[2 * i + 1] += c * __uint_as_float((unsigned)(ov[u][i] >> 32));
+        }
+      }
+      M = Mr;
+    }
+    store_out((size_t)st.s * a.num_q_heads + st.h0 + head, acc, L);
+  };
+
+  // Ring of RING tile buffers: block m + RING - 1 is loading while block m is computed.
   u32x4 kr[RING][NQ], vr[RING][NV];
-  auto issue = [&](int j, u32x4* kd, u32x4* vd) {
-    const int b = __builtin_amdgcn_readlane(bids, j);
-    const char* kp = kbase + (size_t)b * blk_stride;
-    const char* vp = vbase + (size_t)b * blk_stride;
+  auto issue = [&](int m, u32x4* kd, u32x4* vd) {
+    const unsigned t = tile_of(m);
+    const char* kp = kbase + (size_t)t * kTileBytes;
+    const char* vp = vbase + (size_t)t * kTileBytes;
 #pragma unroll
     for (int c = 0; c < NQ; ++c) kd[c] = load16_stream(kp + c * 1024);
 #pragma unroll
     for (int c = 0; c < NV; ++c) vd[c] = load16_stream(vp + c * 1024);
   };
 
-  auto process = [&](const u32x4* kc, u32x4* vc, int j) {
+  auto process = [&](const u32x4* kc, u32x4* vc, int m) {
+    if ((m & 63) == 0 && (m >> 6) != chunk_a) {  // next window of tile ids
+      win_a = win_b;
+      chunk_a = m >> 6;
+      if ((chunk_a + 1) * 64 < mw) {
+        win_b = window(chunk_a + 1);
+        wait_vmem();
+      }
+    }
+    const int p = r0 + wave + kWaves * m;
+    while (p >= cur.end) finish_stream();
+    const int j = p - cur.start;  // block of the stream
+
     // Scores: lane holds S[token 4kg + e][head hl], e = 0..3.
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NQ; ++c) sc = E::qk(kc[c], qv[c], sc);
 
-    const int tb = tok0 + j * kBlock + 4 * kg;  // token of element e = 0
+    const int tb = j * kBlock + 4 * kg;  // token of element e = 0
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = (tb + e < tok1) ? sc[e] * a.scale_log2 : -INFINITY;
+    for (int e = 0; e < 4; ++e) x[e] = (tb + e < cur.n) ? sc[e] * a.scale_log2 : -INFINITY;
     const float lmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
 
     if (__any(lmax > m_run + kLazyRescale)) {
@@ -221,17 +575,17 @@ paged_decode_kernel(DecodeLaunch a) {
       m_run = m_new;
     }
 
-    float p[4];
+    float pr[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
-    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     u32x2 phi, plo;
-    E::split(p, phi, plo);
+    E::split(pr, phi, plo);
 
     // Ragged last block: zero V of dead slots (they may hold anything, NaN included).
-    if (tok0 + (j + 1) * kBlock > tok1) {
-      const unsigned m01 = (tb + 0 < tok1 ? 0x0000FFFFu : 0u) | (tb + 1 < tok1 ? 0xFFFF0000u : 0u);
-      const unsigned m23 = (tb + 2 < tok1 ? 0x0000FFFFu : 0u) | (tb + 3 < tok1 ? 0xFFFF0000u : 0u);
+    if ((j + 1) * kBlock > cur.n) {
+      const unsigned m01 = (tb + 0 < cur.n ? 0x0000FFFFu : 0u) | (tb + 1 < cur.n ? 0xFFFF0000u : 0u);
+      const unsigned m23 = (tb + 2 < cur.n ? 0x0000FFFFu : 0u) | (tb + 3 < cur.n ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
         vc[c].x &= m01;
@@ -251,14 +605,14 @@ paged_decode_kernel(DecodeLaunch a) {
     }
   };
 
-  // Prologue: blocks 0 .. RING-2 in flight.
+  // Prologue: blocks 0 .. RING-2 in flight. Issued unconditionally so that every path into the
+  // steady loop has the same loads outstanding (a wave with fewer blocks reads tile 0, the
+  // window's value past the range, and never uses it).
 #pragma unroll
-  for (int u = 0; u < RING - 1; ++u) {
-    if (u < nblk) issue(u, kr[u], vr[u]);
-  }
-  // Steady state: every iteration issues one block and computes one, with no conditions, so
-  // the compiler can count outstanding loads exactly.
-  const int steady = nblk >= RING - 1 ? (nblk - (RING - 1)) / RING * RING : 0;
+  for (int u = 0; u < RING - 1; ++u) issue(u, kr[u], vr[u]);
+  // Steady state: every iteration issues one block and computes one, with no conditions on the
+  // loads, so the compiler can count outstanding loads exactly.
+  const int steady = mw >= RING - 1 ? (mw - (RING - 1)) / RING * RING : 0;
   for (int j0 = 0; j0 < steady; j0 += RING) {
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
@@ -269,143 +623,53 @@ paged_decode_kernel(DecodeLaunch a) {
   // Tail: at most 2*RING - 2 blocks; block steady + u sits in slot u % RING.
 #pragma unroll
   for (int u = 0; u < 2 * RING - 2; ++u) {
-    const int j = steady + u;
-    if (j < nblk) {
-      if (j + RING - 1 < nblk) {
-        issue(j + RING - 1, kr[(u + RING - 1) % RING], vr[(u + RING - 1) % RING]);
+    const int m = steady + u;
+    if (m < mw) {
+      if (m + RING - 1 < mw) {
+        issue(m + RING - 1, kr[(u + RING - 1) % RING], vr[(u + RING - 1) % RING]);
       }
-      process(kr[u % RING], vr[u % RING], j);
+      process(kr[u % RING], vr[u % RING], m);
     }
   }
+  // Streams of the range this wave has no further blocks of (every wave joins every combine).
+  while (cur.start < r1) finish_stream();
 
-  // Row sums of head hl over the four lane quarters.
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-
-  // Combine the workgroup's waves: O_wg = sum_w 2^(m_w - M) O_w, L = sum_w 2^(m_w - M) l_w.
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-#pragma unroll
-    for (int i = 0; i < NO; ++i) sm_o[wave][4 * kg + e][16 * i + hl] = o[i][e];
-  }
-  if (kg == 0) {
-    sm_m[wave][hl] = m_run;
-    sm_l[wave][hl] = l_tot;
-  }
-  __syncthreads();
-
-  constexpr int kHeadsPerWave = kMaxGroupTile / kWaves;   // 4
-  constexpr int kLanesPerHead = 64 / kHeadsPerWave;       // 16
-  constexpr int kDims = D / kLanesPerHead;                // 8 (d128) or 4 (d64)
-  const int head = wave * kHeadsPerWave + lane / kLanesPerHead;
-  const int d0 = (lane % kLanesPerHead) * kDims;
-  if (head >= nvalid) return;
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][head]);
-  float L = 0.f;
-  float acc[kDims];
-#pragma unroll
-  for (int i = 0; i < kDims; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = sm_m[w][head];
-    const float c = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);  // empty wave -> 0
-    L += c * sm_l[w][head];
-#pragma unroll
-    for (int i = 0; i < kDims; ++i) acc[i] += c * sm_o[w][head][d0 + i];
-  }
-  const size_t row = (size_t)s * a.num_q_heads + h0 + head;
-  if (nparts == 1) {
-    const float inv = L > 0.f ? 1.f / L : 0.f;   // n == 0 -> zeros
-    unsigned short r[kDims];
-#pragma unroll
-    for (int i = 0; i < kDims; ++i) r[i] = E::store(acc[i] * inv);
-    unsigned short* dst = (unsigned short*)a.out + row * D + d0;
-    if constexpr (kDims == 8) {
-      *(u32x4*)dst = u32x4{r[0] | (unsigned)r[1] << 16, r[2] | (unsigned)r[3] << 16,
-                           r[4] | (unsigned)r[5] << 16, r[6] | (unsigned)r[7] << 16};
-    } else {
-      *(u32x2*)dst = u32x2{r[0] | (unsigned)r[1] << 16, r[2] | (unsigned)r[3] << 16};
+  // ---- Publish the split streams (uniform: every wave saw the same ones). ----
+  if (has0 || has1) {
+    wait_vmem();  // the partials are complete at the coherence point before they are counted
+    __syncthreads();
+    if (tid < 2 && (tid == 0 ? has0 : has1)) {
+      const int st_start = tid == 0 ? split0.start : split1.start;
+      const int st_end = tid == 0 ? split0.end : split1.end;
+      const int wa = range_owner(st_start, nwg, W);
+      const int wb = range_owner(st_end - 1, nwg, W);
+      const unsigned old = atomicAdd(a.counters + wa, 1u);
+      const int last = old == (unsigned)(wb - wa);
+      if (last) __hip_atomic_store(a.counters + wa, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last[tid] = last;
     }
-  } else {
-    float* w = a.ws_o + (row * a.max_parts + part) * D + d0;
-#pragma unroll
-    for (int i = 0; i < kDims; ++i) w[i] = acc[i];
-    if (lane % kLanesPerHead == 0) {
-      float* ml = a.ws_ml + (row * a.max_parts + part) * 2;
-      ml[0] = M;
-      ml[1] = L;
-    }
+    __syncthreads();
+    if (has0 && s_last[0]) merge_stream(split0);
+    if (has1 && s_last[1]) merge_stream(split1);
   }
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Log-sum-exp merge of the partitions of one (sequence, query head).
-template <int D, bool BF16>
-__global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch a) {
-  using E = Elem<BF16>;
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x;
-  const int s = blockIdx.x / a.num_q_heads;
-  const int h = blockIdx.x % a.num_q_heads;
-  const int n = a.context_lens[s];
-  const int nparts = partitions_of(n, a.part_blocks, a.max_parts);
-  if (nparts <= 1) return;
-  const size_t base = ((size_t)s * a.num_q_heads + h) * a.max_parts;
-  const float* ml = a.ws_ml + base * 2;
-
-  float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ml[2 * p]);
-  M = wave_max(M);
-  float L = 0.f;
-  for (int p = lane; p < nparts; p += 64) L += __builtin_amdgcn_exp2f(ml[2 * p] - M) * ml[2 * p + 1];
-  L = wave_sum(L);
-
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  const float* op = a.ws_o + base * D + lane * PER;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = __builtin_amdgcn_exp2f(ml[2 * p] - M);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += w * op[(size_t)p * D + i];
-  }
-  const float inv = 1.f / L;
-  unsigned short* out = (unsigned short*)a.out + ((size_t)s * a.num_q_heads + h) * D + lane * PER;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) out[i] = E::store(acc[i] * inv);
 }
 
 template <int D, bool BF16>
-hipError_t launch_typed(const DecodeLaunch& a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads * a.head_tiles), (unsigned)a.max_parts);
-  hipLaunchKernelGGL((paged_decode_kernel<D, BF16, kRing<D>>), grid, dim3(64 * kWaves), 0, stream,
-                     a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.max_parts <= 1) return err;
-  hipLaunchKernelGGL((merge_kernel<D, BF16>), dim3((unsigned)(a.num_seqs * a.num_q_heads)),
-                     dim3(64), 0, stream, a);
+hipError_t launch_typed(const DecodeLaunch& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_decode_kernel<D, BF16, kRing<D>>), dim3((unsigned)grid),
+                     dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeLaunch& a, int head_dim, bool bf16, hipStream_t stream) {
+hipError_t launch_decode(const DecodeLaunch& a, int grid, int head_dim, bool bf16,
+                         hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
-  if (head_dim == 128) return bf16 ? launch_typed<128, true>(a, stream) : launch_typed<128, false>(a, stream);
-  return bf16 ? launch_typed<64, true>(a, stream) : launch_typed<64, false>(a, stream);
+  if (head_dim == 128) {
+    return bf16 ? launch_typed<128, true>(a, grid, stream) : launch_typed<128, false>(a, grid, stream);
+  }
+  return bf16 ? launch_typed<64, true>(a, grid, stream) : launch_typed<64, false>(a, grid, stream);
 }
 
 }  // namespace pkv

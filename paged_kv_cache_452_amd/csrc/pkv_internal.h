@@ -10,8 +10,8 @@ namespace pkv {
 constexpr int kBlock = 16;          // tokens per physical block this build supports
 constexpr int kMaxGroupTile = 16;   // query heads per wave (matrix-core N dimension)
 constexpr int kWaves = 4;           // wavefronts per decode workgroup
-constexpr int kWaveBlocks = 64;     // blocks one wavefront handles at most (ids in one VGPR)
-constexpr int kMaxPartBlocks = kWaves * kWaveBlocks;  // blocks per workgroup (partition)
+constexpr int kMaxSeqs = 2048;      // sequences one decode launch plans for (LDS prefix sums)
+constexpr int kWorkgroupsPerCU = 2; // resident decode workgroups per compute unit
 
 struct DecodeLaunch {
   void* out;
@@ -20,8 +20,9 @@ struct DecodeLaunch {
   const void* v_pool;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_o;          // [S][Hq][max_parts][D] unnormalised partial outputs
-  float* ws_ml;         // [S][Hq][max_parts][2] (running max in log2 units, row sum)
+  unsigned* counters;   // [grid] arrival counts of split streams; zero between launches
+  float* ws_o;          // [grid][2][16][D] unnormalised partial outputs of split streams
+  float* ws_ml;         // [grid][2][16][2] (reference max in log2 units, row sum)
   float scale_log2;     // scale * log2(e)
   int num_seqs;
   int num_q_heads;
@@ -29,13 +30,12 @@ struct DecodeLaunch {
   int group;            // num_q_heads / num_kv_heads
   int head_tiles;       // ceil(group / 16)
   int max_blocks;       // block table row length
-  int part_blocks;      // most blocks of one partition (<= kMaxPartBlocks); a sequence of nb
-                        // blocks has ceil(nb / part_blocks) partitions of near-equal length
-  int max_parts;        // partitions of the longest allowed sequence
+  int max_tokens;       // max_blocks * 16: context lengths are clamped to it
 };
 
-// Launch the decode kernel (and the merge when max_parts > 1). Returns a hipError_t.
-hipError_t launch_decode(const DecodeLaunch& a, int head_dim, bool bf16, hipStream_t stream);
+// Launch the decode kernel on `grid` workgroups. Returns a hipError_t.
+hipError_t launch_decode(const DecodeLaunch& a, int grid, int head_dim, bool bf16,
+                         hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,

@@ -37,15 +37,17 @@ def oracle_dtype(t: torch.Tensor) -> int:
 
 
 def gpu_decode(q, k_layer, v_layer, block_tables, context_lens, scale, Hq, Hkv, max_ctx,
-               partition_tokens=0, out=None):
+               num_workgroups=0, out=None, workspace=None):
+    """Run the HIP decode; a fresh zeroed workspace unless one is passed in."""
     D = q.shape[-1]
     S = q.shape[0]
     if out is None:
         out = torch.empty_like(q)
-    nbytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, max_ctx, partition_tokens)
-    ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device) if nbytes else None
+    if workspace is None:
+        nbytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, max_ctx, num_workgroups)
+        workspace = pkv.new_workspace(nbytes, q.device)
     pkv.paged_attention_decode(out, q, k_layer, v_layer, block_tables, context_lens, scale, Hq,
-                               Hkv, D, 16, max_ctx, partition_tokens, ws)
+                               Hkv, D, 16, max_ctx, num_workgroups, workspace)
     return out
 
 

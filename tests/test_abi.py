@@ -78,12 +78,17 @@ def test_kv_pool_create_and_layers():
 
 def _decode(lib, **kw):
     args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, scale=0.1, hq=32, hkv=8,
-                d=128, b=16, s=4, mb=8, maxc=128, pt=0, dt=0, ws=None, wsb=0)
+                d=128, b=16, s=4, mb=8, maxc=128, nwg=1, dt=0, ws=None, wsb=0)
     args.update(kw)
     return lib.paged_attention_decode(args["out"], args["q"], args["k"], args["v"], args["bt"],
                                       args["cl"], args["scale"], args["hq"], args["hkv"],
                                       args["d"], args["b"], args["s"], args["mb"], args["maxc"],
-                                      args["pt"], args["dt"], args["ws"], args["wsb"], None)
+                                      args["nwg"], args["dt"], args["ws"], args["wsb"], None)
+
+
+def _ws(G, D=128):
+    """G ranges x 2 partials x 16 heads x (D + 2) floats, then G counters (256-rounded)."""
+    return G * 2 * 16 * (D + 2) * 4 + -(-4 * G // 256) * 256
 
 
 def test_decode_argument_errors_return_before_launch():
@@ -93,40 +98,45 @@ def test_decode_argument_errors_return_before_launch():
     assert _decode(lib, d=96) == UNSUPPORTED
     assert _decode(lib, b=32) == UNSUPPORTED
     assert _decode(lib, dt=5) == UNSUPPORTED
-    assert _decode(lib, q=None) == INVALID
+    assert _decode(lib, q=None, ws=FAKE, wsb=1 << 30) == INVALID
     assert _decode(lib, out=FAKE + 2) == ALIGN
     assert _decode(lib, k=FAKE + 8) == ALIGN
     assert _decode(lib, bt=FAKE + 2) == ALIGN
     assert _decode(lib, maxc=129, mb=8) == INVALID          # more than the table can hold
-    assert _decode(lib, pt=24) == INVALID                   # not a multiple of the block size
+    assert _decode(lib, nwg=-1) == INVALID                  # negative workgroup count
+    assert _decode(lib, nwg=(1 << 20) + 1) == INVALID
     assert _decode(lib, scale=float("nan")) == INVALID
     assert _decode(lib, s=-1) == INVALID
     assert _decode(lib, s=0) == OK                          # nothing to do, nothing launched
-    # a split partition needs a workspace
-    assert _decode(lib, maxc=128, pt=32, ws=None, wsb=0) == WORKSPACE
+    assert _decode(lib, s=2049) == UNSUPPORTED              # beyond the per-launch plan size
+    assert _decode(lib, s=4, mb=(1 << 28)) == UNSUPPORTED   # positions beyond 32 bits
+    # every launch needs a workspace (counters + partials of its workgroup ranges)
+    assert _decode(lib, nwg=32, ws=None, wsb=0) == WORKSPACE
     need = pkv.paged_attention_workspace_bytes(4, 32, 8, 128, 16, 128, 32)
-    assert need == 4 * 32 * 4 * (128 + 2) * 4
-    assert _decode(lib, maxc=128, pt=32, ws=FAKE, wsb=need - 1) == WORKSPACE
-    assert _decode(lib, maxc=128, pt=32, ws=FAKE + 4, wsb=need) == ALIGN
+    assert need == _ws(32)
+    assert _decode(lib, nwg=32, ws=FAKE, wsb=need - 1) == WORKSPACE
+    assert _decode(lib, nwg=32, ws=FAKE + 16, wsb=need) == ALIGN
 
 
-def test_workspace_and_partition_choice():
-    # one partition covers everything -> no workspace
-    assert pkv.paged_attention_workspace_bytes(4, 32, 8, 128, 16, 100, 0) == 0
-    assert pkv.paged_attention_workspace_bytes(4, 32, 8, 128, 16, 100, 256) == 0
-    assert pkv.paged_attention_workspace_bytes(0, 32, 8, 128, 16, 0, 0) == 0
+def test_workspace_and_workgroup_choice():
     with pytest.raises(pkv.PagedKVError):
         pkv.paged_attention_workspace_bytes(4, 30, 8, 128, 16, 100, 0)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.paged_attention_workspace_bytes(4, 32, 8, 128, 16, 100, -3)
+    for G in (1, 2, 100, 512, 1000, 1 << 20):
+        assert pkv.paged_attention_workspace_bytes(64, 64, 8, 128, 16, 4096, G) == _ws(G)
+        assert pkv.paged_attention_workspace_bytes(64, 64, 8, 64, 16, 4096, G) == _ws(G, 64)
     for S, Hq, Hkv, maxc in [(64, 64, 8, 4096), (64, 32, 8, 8192), (32, 40, 40, 2048),
                              (66, 32, 8, 32768), (4, 4, 4, 41), (1, 8, 1, 1 << 20)]:
-        pt = pkv.paged_attention_partition_tokens(S, Hq, Hkv, maxc, 16)
-        assert pt > 0 and pt % 16 == 0
-        parts = max(1, math.ceil(maxc / pt))
-        ws = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, 128, 16, maxc, 0)
-        assert ws == (0 if parts == 1 else S * Hq * parts * 130 * 4)
-        assert parts <= 65535
-    assert pkv.paged_attention_partition_tokens(4, 4, 4, 41, 16) == 48   # single pass, 3 blocks
-    assert pkv.paged_attention_partition_tokens(4, 30, 8, 41, 16) == 0
+        g = pkv.paged_attention_num_workgroups(S, Hq, Hkv, maxc, 16)
+        heads_tiles = -(-(Hq // Hkv) // 16)
+        positions = S * Hkv * heads_tiles * -(-maxc // 16)
+        assert 1 <= g <= max(1, -(-positions // 64))
+        assert g <= 2 * 304   # two resident workgroups per compute unit
+        assert pkv.paged_attention_workspace_bytes(S, Hq, Hkv, 128, 16, maxc, 0) == _ws(g)
+    # tiny batch: 4 sequences x 3 blocks x 4 kv heads = 48 positions -> 1 workgroup
+    assert pkv.paged_attention_num_workgroups(4, 4, 4, 41, 16) == 1
+    assert pkv.paged_attention_num_workgroups(4, 30, 8, 41, 16) == 0
 
 
 def test_reshape_argument_errors():

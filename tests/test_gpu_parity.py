@@ -94,8 +94,7 @@ def test_config4_all_80_layers_sampled():
     batch = workloads.make_batch(spec, device=DEV, tables=t)
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     outs = torch.empty((spec.num_layers, S, Hq, D), dtype=batch.q.dtype, device=DEV)
-    ws_bytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, 4096)
-    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=DEV)
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, 4096), DEV)
     say("config 4: decode 80 layers")
     for L in range(spec.num_layers):
         k, v = _layer(batch, L)
@@ -150,29 +149,58 @@ def test_edge_shapes(Hq, Hkv, D, dtype, lens):
             assert torch.count_nonzero(out[s]).item() == 0
 
 
-@pytest.mark.parametrize("partition_tokens", [16, 32, 256, 512, 4096, 0])
-def test_partition_sizes_agree_with_oracle(partition_tokens):
+@pytest.mark.parametrize("num_workgroups", [1, 2, 3, 7, 64, 500, 2000, 0])
+def test_workgroup_counts_agree_with_oracle(num_workgroups):
+    """Any number of workgroups gives the oracle's result: 1 (no stream split), a few (long
+    ranges crossing many streams), many more than positions (most streams cut into one-block
+    pieces merged by the last arriver)."""
     spec, t, b = _random_case(32, 8, 128, [1, 255, 256, 257, 1500, 4000], seed=11)
     k, v = _layer(b)
-    say("partition", partition_tokens)
+    say("workgroups", num_workgroups)
     out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, 4000,
-                     partition_tokens)
+                     num_workgroups)
     torch.cuda.synchronize()
     ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 32, 8,
                         t.num_blocks)
-    assert_close(out, ref, f"partition {partition_tokens}")
+    assert_close(out, ref, f"{num_workgroups} workgroups")
 
 
-def test_long_sequence_many_partitions():
+def test_workspace_counters_return_to_zero_and_reuse():
+    """The arrival counters are left zero by every call, so one workspace serves call after call
+    (different batches, different workgroup counts) with identical results."""
+    spec, t, b = _random_case(32, 8, 128, [3000, 17, 900, 4096, 1], seed=14)
+    k, v = _layer(b)
+    G = 300
+    nbytes = pkv.paged_attention_workspace_bytes(5, 32, 8, 128, 16, 4096, G)
+    ws = pkv.new_workspace(nbytes, DEV)
+    counters = ws[-G:]   # the last G words; calls with fewer workgroups use a suffix of them
+    ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 32, 8,
+                        t.num_blocks)
+    first = None
+    for rep, g in enumerate([G, G, 77, G]):
+        say("reuse", rep, g)
+        out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, 4096, g,
+                         workspace=ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(counters).item()) == 0, "counters not reset"
+        assert_close(out, ref, f"reuse {rep}")
+        if g == G:
+            if first is None:
+                first = out.clone()
+            else:
+                assert torch.equal(first.view(torch.int16), out.view(torch.int16))
+
+
+def test_long_sequence_spread_over_workgroups():
     spec, t, b = _random_case(32, 8, 128, [32768, 100], seed=12)
     k, v = _layer(b)
-    for pt in (256, 0):
-        say("long sequence, partition", pt)
-        out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, 32768, pt)
+    for g in (1, 16, 0):
+        say("long sequence, workgroups", g)
+        out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, 32768, g)
         torch.cuda.synchronize()
         ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 32, 8,
                             t.num_blocks)
-        assert_close(out, ref, f"32k partition {pt}")
+        assert_close(out, ref, f"32k, {g} workgroups")
 
 
 def test_max_context_fills_block_table():
