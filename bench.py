@@ -100,6 +100,68 @@ def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3) -> int:
     return 0
 
 
+def bench_copy_blocks(args) -> int:
+    """Copy-on-write block copies on the 70B-shaped pool: 64 pairs (one per sequence of the
+    batch), every layer, K and V. Bytes = 2 (read + write) x pairs x layers x 2 x block bytes."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_452_amd as pkv
+    import workloads
+
+    spec = workloads.SPECS[4]
+    L, NB, Hkv, D = spec.num_layers, 16384, spec.num_kv_heads, spec.head_dim
+    k = torch.empty((L, NB, Hkv, 16 * D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    k.view(torch.int16).random_(-32768, 32767)
+    v.view(torch.int16).random_(-32768, 32767)
+    pool = pkv.kv_pool_create(k, v, k.numel() * 2, L, NB, Hkv, D, 16, pkv.PKV_BF16)
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(NB).astype(np.int32)
+    npairs = 64
+    src = torch.from_numpy(perm[:npairs].copy()).cuda()
+    dst = torch.from_numpy(perm[npairs:2 * npairs].copy()).cuda()
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pkv.copy_blocks(pool, src, dst, stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        pkv.copy_blocks(pool, src, dst, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    block_bytes = Hkv * 16 * D * 2
+    moved = 2 * npairs * L * 2 * block_bytes
+    gbs = moved / (us * 1e-6) / 1e9
+    # CPU oracle beside it: the same copies as numpy block assignments on host copies of 8 layers.
+    kh = k[:8].view(torch.int16).cpu().numpy()
+    vh = v[:8].view(torch.int16).cpu().numpy()
+    s_np, d_np = perm[:npairs], perm[npairs:2 * npairs]
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 2.0:
+        kh[:, d_np] = kh[:, s_np]
+        vh[:, d_np] = vh[:, s_np]
+        reps += 1
+    cpu_s = (time.perf_counter() - t0) / reps
+    cpu_gbs = 2 * npairs * 8 * 2 * block_bytes / cpu_s / 1e9
+    print(json.dumps({
+        "metric": "copy_blocks GB/s (read + write, % of MI355X HBM peak)", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "us_per_call": round(us, 2), "higher_is_better": True, "data": "synthetic",
+        "dtype": "bf16",
+        "config": {"workload": "copy-on-write burst on the 70B-shaped pool: 64 block copies x "
+                               "80 layers x (K, V), 32 KiB per block region",
+                   "bytes_per_call": moved},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                         "sample": "numpy block copies of the same 64 pairs on host copies of 8 "
+                                   "layers, single thread"}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +175,8 @@ def main() -> int:
                          "data keep a small single-layer workload from being served out of the "
                          "256 MB last-level cache between launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel", choices=["decode", "copy_blocks"], default="decode",
+                    help="decode (the hot path, default) or copy_blocks (copy-on-write copies)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -127,6 +191,8 @@ def main() -> int:
 
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.kernel == "copy_blocks":
+        return bench_copy_blocks(args)
     pkv.load_library()
     dev = "cuda"
     spec = workloads.SPECS[args.config]

@@ -82,7 +82,8 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = -2, /* head_dim / block_size / dtype this build has no kernel for */
   PKV_ERR_ALIGNMENT = -3,   /* a device pointer not 16-byte aligned */
   PKV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than paged_attention_workspace_bytes */
-  PKV_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+  PKV_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
+  PKV_ERR_NO_BLOCKS = -6    /* the block manager's free list cannot supply the blocks needed */
 } pkv_status;
 
 typedef enum { PKV_BF16 = 0, PKV_FP16 = 1 } pkv_dtype;
@@ -192,6 +193,78 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
                                   int block_size, int num_seqs, int max_blocks_per_seq,
                                   int max_context_len, int num_workgroups, pkv_dtype dtype,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Copy-on-write block copies: for each i in [0, num_copies), block src_blocks[i] is copied to
+ * block dst_blocks[i] in the K and the V pool of every layer of `pool` (all kv heads, all
+ * block_size token slots), bit-exact. This is the device half of copy-on-write ("PagedAttention
+ * and KV Cache Management" (blog.sejan.dev), section "Advanced Memory Sharing: Prefix Caching &
+ * Copy-on-Write", part 2: a fresh block receives a copy of the shared block before the writer's
+ * table points at it). Run it before the reshape_and_cache that writes into the copies.
+ *   src_blocks, dst_blocks  device int32 [num_copies], 4-byte aligned, ids in [0, num_blocks).
+ *                           A destination must not appear twice or also be a source (the order
+ *                           of the copies is not defined). Not validated on the device.
+ * num_copies in [0, 65535]; 0 is a no-op.
+ */
+pkv_status copy_blocks(const pkv_pool* pool, const int32_t* src_blocks, const int32_t* dst_blocks,
+                       int num_copies, hipStream_t stream);
+
+/*
+ * Host block manager: the bookkeeping of which physical blocks hold which sequence's tokens
+ * ("PagedAttention and KV Cache Management" (blog.sejan.dev), sections "How Block Paging Operates
+ * During Generation" (on-demand and boundary allocation), "Advanced Memory Sharing: Prefix Caching
+ * & Copy-on-Write" (fork by reference counts, copy-on-write) and "Hands-On Implementation:
+ * Building a PagedAttention Block Allocator in Python" (free blocks are handed out from the front
+ * of the free list and returned to its back; running out is an error)).
+ * It works on host memory only. A decode step calls kv_block_manager_append for its new tokens,
+ * then copy_blocks of the returned pairs, reshape_and_cache into the returned slots, and
+ * paged_attention_decode with the tables of kv_block_manager_tables. Sequences are named by
+ * caller-chosen int64 ids. Every call succeeds completely or changes nothing. An object is not
+ * thread-safe: one caller at a time.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager of num_blocks blocks of block_size tokens, all free (free list 0, 1, 2, ...). */
+pkv_status kv_block_manager_create(pkv_block_manager** out, int num_blocks, int block_size);
+void kv_block_manager_destroy(pkv_block_manager* bm);  /* NULL is a no-op */
+/* Free blocks, or -1 for NULL. */
+int kv_block_manager_num_free(const pkv_block_manager* bm);
+
+/* New sequence seq_id holding a prompt of num_tokens tokens: ceil(num_tokens / block_size)
+ * blocks taken from the front of the free list. PKV_ERR_INVALID_ARG if seq_id exists,
+ * PKV_ERR_NO_BLOCKS if the free list is too short. */
+pkv_status kv_block_manager_allocate(pkv_block_manager* bm, int64_t seq_id, int64_t num_tokens);
+
+/* New sequence dst_seq_id sharing every block (and the token count) of src_seq_id; each shared
+ * block's reference count grows by one. No block is taken or copied. */
+pkv_status kv_block_manager_fork(pkv_block_manager* bm, int64_t src_seq_id, int64_t dst_seq_id);
+
+/*
+ * One new token for each of seq_ids[0..num_seqs) (in order; an id may repeat). For token i,
+ * slot_mapping[i] receives its slot (block * block_size + offset). A token that starts a new
+ * logical block takes a block from the free list. A token written into a block that other
+ * sequences still reference takes a fresh block; the pair (shared block, fresh block) is
+ * appended to copy_src / copy_dst (host arrays of capacity num_seqs), and *num_copies is set to
+ * the number of pairs. PKV_ERR_NO_BLOCKS (and no change at all) if the batch needs more blocks
+ * than are free; PKV_ERR_INVALID_ARG for an unknown id.
+ */
+pkv_status kv_block_manager_append(pkv_block_manager* bm, const int64_t* seq_ids, int num_seqs,
+                                   int64_t* slot_mapping, int32_t* copy_src, int32_t* copy_dst,
+                                   int* num_copies);
+
+/* The sequence ends: each of its blocks loses one reference; blocks at zero go to the back of
+ * the free list, in table order. */
+pkv_status kv_block_manager_release(pkv_block_manager* bm, int64_t seq_id);
+
+/*
+ * Decode inputs for seq_ids[0..num_seqs): row i of block_tables (host int32
+ * [num_seqs][max_blocks_per_seq]) receives sequence i's physical blocks, padded with -1, and
+ * context_lens[i] its token count. PKV_ERR_INVALID_ARG (nothing written) for an unknown id or a
+ * table longer than max_blocks_per_seq.
+ */
+pkv_status kv_block_manager_tables(const pkv_block_manager* bm, const int64_t* seq_ids,
+                                   int num_seqs, int max_blocks_per_seq, int32_t* block_tables,
+                                   int32_t* context_lens);
 
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(pkv_status status);

@@ -20,7 +20,12 @@ PKV_FP16 = 1
 
 EXPORTED = ("kv_pool_bytes", "kv_pool_create", "kv_pool_layer", "kv_pool_destroy",
             "reshape_and_cache", "paged_attention_num_workgroups",
-            "paged_attention_workspace_bytes", "paged_attention_decode", "pkv_status_string")
+            "paged_attention_workspace_bytes", "paged_attention_decode", "copy_blocks",
+            "kv_block_manager_create", "kv_block_manager_destroy", "kv_block_manager_num_free",
+            "kv_block_manager_allocate", "kv_block_manager_fork", "kv_block_manager_append",
+            "kv_block_manager_release", "kv_block_manager_tables", "pkv_status_string")
+
+PKV_ERR_NO_BLOCKS = -6
 
 
 class PagedKVError(RuntimeError):
@@ -61,6 +66,25 @@ def load_library(build_if_missing: bool = True):
     lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, i,
                                            vp, sz, vp]
     lib.paged_attention_decode.restype = i
+    lib.copy_blocks.argtypes = [vp, vp, vp, i, vp]
+    lib.copy_blocks.restype = i
+    i64 = ctypes.c_int64
+    lib.kv_block_manager_create.argtypes = [ctypes.POINTER(vp), i, i]
+    lib.kv_block_manager_create.restype = i
+    lib.kv_block_manager_destroy.argtypes = [vp]
+    lib.kv_block_manager_destroy.restype = None
+    lib.kv_block_manager_num_free.argtypes = [vp]
+    lib.kv_block_manager_num_free.restype = i
+    lib.kv_block_manager_allocate.argtypes = [vp, i64, i64]
+    lib.kv_block_manager_allocate.restype = i
+    lib.kv_block_manager_fork.argtypes = [vp, i64, i64]
+    lib.kv_block_manager_fork.restype = i
+    lib.kv_block_manager_append.argtypes = [vp, vp, i, vp, vp, vp, ctypes.POINTER(i)]
+    lib.kv_block_manager_append.restype = i
+    lib.kv_block_manager_release.argtypes = [vp, i64]
+    lib.kv_block_manager_release.restype = i
+    lib.kv_block_manager_tables.argtypes = [vp, vp, i, i, vp, vp]
+    lib.kv_block_manager_tables.restype = i
     lib.pkv_status_string.argtypes = [i]
     lib.pkv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -212,6 +236,84 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
         float(scale), num_q_heads, num_kv_heads, head_dim, block_size, S, max_blocks,
         max_context_len, num_workgroups, _dtype_code(q), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def copy_blocks(pool: "KVPool", src_blocks, dst_blocks, stream=None) -> None:
+    """Copy blocks src_blocks[i] -> dst_blocks[i] (device int32 tensors) in every layer of the
+    pool's K and V (the device half of copy-on-write)."""
+    _require_cuda(src_blocks, dst_blocks)
+    n = int(src_blocks.numel())
+    if int(dst_blocks.numel()) != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    _check("copy_blocks", load_library().copy_blocks(pool._h, _ptr(src_blocks) if n else None,
+                                                     _ptr(dst_blocks) if n else None, n,
+                                                     _stream(stream) if n else None))
+
+
+class BlockManager:
+    """Host block manager (kv_block_manager_*): blocks of one pool, per-sequence tables, fork and
+    copy-on-write. Plain numpy in and out; no device work."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check("kv_block_manager_create", lib.kv_block_manager_create(ctypes.byref(h), num_blocks,
+                                                                      block_size))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        try:
+            if self._h is not None and self._h.value:
+                load_library().kv_block_manager_destroy(self._h)
+            self._h = None
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return int(load_library().kv_block_manager_num_free(self._h))
+
+    def allocate(self, seq_id: int, num_tokens: int) -> None:
+        _check("kv_block_manager_allocate",
+               load_library().kv_block_manager_allocate(self._h, seq_id, num_tokens))
+
+    def fork(self, src_seq_id: int, dst_seq_id: int) -> None:
+        _check("kv_block_manager_fork",
+               load_library().kv_block_manager_fork(self._h, src_seq_id, dst_seq_id))
+
+    def release(self, seq_id: int) -> None:
+        _check("kv_block_manager_release", load_library().kv_block_manager_release(self._h, seq_id))
+
+    def append(self, seq_ids):
+        """One new token per listed sequence. Returns (slot_mapping int64 [n],
+        copies int32 [k][2] of (shared block, fresh block))."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        n = ids.shape[0]
+        slots = np.zeros(n, np.int64)
+        src = np.zeros(max(n, 1), np.int32)
+        dst = np.zeros(max(n, 1), np.int32)
+        k = ctypes.c_int(0)
+        vp = ctypes.c_void_p
+        _check("kv_block_manager_append", load_library().kv_block_manager_append(
+            self._h, ids.ctypes.data_as(vp), n, slots.ctypes.data_as(vp), src.ctypes.data_as(vp),
+            dst.ctypes.data_as(vp), ctypes.byref(k)))
+        return slots, np.stack([src[:k.value], dst[:k.value]], axis=1)
+
+    def tables(self, seq_ids, max_blocks_per_seq: int):
+        """(block_tables int32 [n][max_blocks_per_seq] padded with -1, context_lens int32 [n])."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        n = ids.shape[0]
+        bt = np.zeros((n, max_blocks_per_seq), np.int32)
+        cl = np.zeros(n, np.int32)
+        vp = ctypes.c_void_p
+        _check("kv_block_manager_tables", load_library().kv_block_manager_tables(
+            self._h, ids.ctypes.data_as(vp), n, max_blocks_per_seq, bt.ctypes.data_as(vp),
+            cl.ctypes.data_as(vp)))
+        return bt, cl
 
 
 class Decoder:

@@ -171,6 +171,20 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* k_pool, v
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+pkv_status copy_blocks(const pkv_pool* pool, const int32_t* src_blocks, const int32_t* dst_blocks,
+                       int num_copies, hipStream_t stream) {
+  if (pool == nullptr || num_copies < 0 || num_copies > 65535) return PKV_ERR_INVALID_ARG;
+  if (num_copies == 0) return PKV_OK;
+  if (src_blocks == nullptr || dst_blocks == nullptr) return PKV_ERR_INVALID_ARG;
+  if (((uintptr_t)src_blocks & 3u) || ((uintptr_t)dst_blocks & 3u)) return PKV_ERR_ALIGNMENT;
+  if (pool->num_layers > 32767) return PKV_ERR_UNSUPPORTED;
+  const size_t block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim * 2;
+  const hipError_t err = pkv::launch_copy_blocks(pool->k, pool->v, pool->layer_bytes, block_bytes,
+                                                 pool->num_layers, src_blocks, dst_blocks,
+                                                 num_copies, stream);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int paged_attention_num_workgroups(int num_seqs, int num_q_heads, int num_kv_heads,
                                    int max_context_len, int block_size) {
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size, 0) ||
@@ -256,6 +270,7 @@ const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_ALIGNMENT: return "PKV_ERR_ALIGNMENT";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_NO_BLOCKS: return "PKV_ERR_NO_BLOCKS";
   }
   return "PKV_UNKNOWN_STATUS";
 }

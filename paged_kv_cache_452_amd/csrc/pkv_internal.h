@@ -37,6 +37,11 @@ struct DecodeLaunch {
 hipError_t launch_decode(const DecodeLaunch& a, int grid, int head_dim, bool bf16,
                          hipStream_t stream);
 
+// Copy the K and V regions of blocks src[i] -> dst[i] in every layer (device arrays).
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, size_t layer_bytes, size_t block_bytes,
+                              int num_layers, const int32_t* src, const int32_t* dst,
+                              int num_copies, hipStream_t stream);
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                                     int head_dim, hipStream_t stream);

@@ -12,7 +12,7 @@ from oracle import sizing
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pagedkv.h")
 
-OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP = 0, -1, -2, -3, -4, -5
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP, NO_BLOCKS = 0, -1, -2, -3, -4, -5, -6
 FAKE = 1 << 40  # a 4 KiB-aligned address that is never dereferenced on these paths
 
 
@@ -34,7 +34,8 @@ def test_library_exports_every_declared_function():
 def test_status_strings():
     for code, name in [(OK, "PKV_OK"), (INVALID, "PKV_ERR_INVALID_ARG"),
                        (UNSUPPORTED, "PKV_ERR_UNSUPPORTED"), (ALIGN, "PKV_ERR_ALIGNMENT"),
-                       (WORKSPACE, "PKV_ERR_WORKSPACE"), (HIP, "PKV_ERR_HIP")]:
+                       (WORKSPACE, "PKV_ERR_WORKSPACE"), (HIP, "PKV_ERR_HIP"),
+                       (NO_BLOCKS, "PKV_ERR_NO_BLOCKS")]:
         assert pkv.pkv_status_string(code) == name
 
 
@@ -156,3 +157,17 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         pkv.paged_attention_decode(q, q, q, q, torch.zeros(1, 1, dtype=torch.int32),
                                    torch.zeros(1, dtype=torch.int32), 0.125, 4, 4, 64, 16, 0)
+
+
+def test_copy_blocks_argument_errors():
+    lib = pkv.load_library()
+    each = pkv.kv_pool_bytes(2, 16, 4, 128, 16, pkv.PKV_BF16)
+    pool = pkv.kv_pool_create(FAKE, FAKE * 2, each, 2, 16, 4, 128, 16, pkv.PKV_BF16)
+    f = lib.copy_blocks
+    assert f(pool._h, None, None, 0, None) == OK            # nothing to copy, nothing launched
+    assert f(None, FAKE, FAKE, 1, None) == INVALID
+    assert f(pool._h, FAKE, FAKE, -1, None) == INVALID
+    assert f(pool._h, FAKE, FAKE, 65536, None) == INVALID
+    assert f(pool._h, None, FAKE, 1, None) == INVALID
+    assert f(pool._h, FAKE + 2, FAKE, 1, None) == ALIGN
+    pool.destroy()
