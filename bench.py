@@ -71,7 +71,8 @@ def cpu_baseline(batch, spec, layers, budget_s=15.0):
         d2h_s += time.perf_counter() - t0
         t0 = time.perf_counter()
         oracle.paged_decode(q, kw, vw, t.block_tables, t.context_lens, spec.scale,
-                            spec.num_q_heads, spec.num_kv_heads, spec.head_dim, 16, t.num_blocks,
+                            spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size,
+                            t.num_blocks,
                             oracle.BF16, threads=threads)
         cpu_s += time.perf_counter() - t0
         done_bytes += per_layer
@@ -170,6 +171,7 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--workgroups", type=int, default=0,
                     help="decode workgroups (0: the library's choice)")
+    ap.add_argument("--block-size", type=int, default=16, choices=[16, 32])
     ap.add_argument("--layers", type=int, default=0,
                     help="layers in the pool (default: the workload's own; more layers of fresh "
                          "data keep a small single-layer workload from being served out of the "
@@ -198,13 +200,16 @@ def main() -> int:
     spec = workloads.SPECS[args.config]
     if args.layers > 0:
         spec = dataclasses.replace(spec, num_layers=args.layers)
+    if args.block_size != spec.block_size:
+        spec = dataclasses.replace(spec, block_size=args.block_size)
+    B = spec.block_size
     t = workloads.make_tables(spec)
     batch = workloads.make_batch(spec, device=dev, tables=t)
     S, Hq, Hkv, D, L = (spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                         spec.num_layers)
     max_ctx = int(t.context_lens.max())
     nwg = args.workgroups
-    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, max_ctx, nwg),
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, B, max_ctx, nwg),
                            dev)
     outs = torch.empty((L, S, Hq, D), dtype=batch.q.dtype, device=dev)
     layers = [(batch.k_pool[i], batch.v_pool[i]) for i in range(L)]
@@ -213,15 +218,15 @@ def main() -> int:
     def step():
         for i, (k, v) in enumerate(layers):
             pkv.reshape_and_cache(batch.new_key, batch.new_value, k, v, batch.slot_mapping,
-                                  t.num_blocks, 16, stream)
+                                  t.num_blocks, B, stream)
             pkv.paged_attention_decode(outs[i], batch.q, k, v, batch.block_tables,
-                                       batch.context_lens, spec.scale, Hq, Hkv, D, 16, max_ctx,
+                                       batch.context_lens, spec.scale, Hq, Hkv, D, B, max_ctx,
                                        nwg, ws, stream)
 
     def sweep_decode():
         for i, (k, v) in enumerate(layers):
             pkv.paged_attention_decode(outs[i], batch.q, k, v, batch.block_tables,
-                                       batch.context_lens, spec.scale, Hq, Hkv, D, 16, max_ctx,
+                                       batch.context_lens, spec.scale, Hq, Hkv, D, B, max_ctx,
                                        nwg, ws, stream)
 
     def timed(fn, reps):
@@ -245,12 +250,13 @@ def main() -> int:
     ms_total = timed(step, args.steps)
     ms_step = ms_total / args.steps
 
-    per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D)
+    per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B)
     value = per_launch * L / (ms_step * 1e-3) / 1e9
     achieved = per_launch / (avg_decode_ms * 1e-3) / 1e9
-    workload = spec.name
+    workload = ((spec.name if args.layers <= 0 else f"{spec.name}, {L} layers") +
+                ("" if B == 16 else f", block size {B}"))
     traffic = measured_traffic(workload)
-    grid = nwg or pkv.paged_attention_num_workgroups(S, Hq, Hkv, max_ctx, 16)
+    grid = nwg or pkv.paged_attention_num_workgroups(S, Hq, Hkv, max_ctx, B)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -264,9 +270,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": spec.dtype,
         "data": "synthetic",
-        "config": {"workload": workload if args.layers <= 0 else f"{workload}, {L} layers", "num_seqs": S, "context_lens": "all 4096" if
+        "config": {"workload": workload, "num_seqs": S, "context_lens": "all 4096" if
                    args.config == 4 else "seeded", "num_q_heads": Hq, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": 16, "num_layers": L,
+                   "head_dim": D, "block_size": B, "num_layers": L,
                    "num_blocks_per_layer": t.num_blocks, "decode_workgroups": grid,
                    "step": "per layer: reshape_and_cache of the step's new tokens + "
                            "paged_attention_decode"},

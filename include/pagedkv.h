@@ -31,7 +31,9 @@
  * Element types: bf16 (PKV_BF16) or IEEE fp16 (PKV_FP16); q, key, value, the pools and out all use
  * the same type. Accumulation is fp32.
  *
- * Supported shapes: head_dim in {64, 128}; block_size == 16; num_q_heads % num_kv_heads == 0
+ * Supported shapes: head_dim in {64, 128}; block_size in {16, 32} ("PagedAttention and KV Cache
+ * Management", section "PagedAttention: OS Virtual Memory Architecture for GPUs": B = 16 or 32);
+ * num_q_heads % num_kv_heads == 0
  * (query head h reads kv head h / (num_q_heads / num_kv_heads): consecutive query heads form one
  * group); any group size.
  *

@@ -24,8 +24,10 @@ struct pkv_pool {
 
 namespace {
 
+bool supported_block(int block_size) { return block_size == 16 || block_size == 32; }
+
 bool supported_shape(int head_dim, int block_size, pkv_dtype dtype) {
-  return (head_dim == 64 || head_dim == 128) && block_size == pkv::kBlock &&
+  return (head_dim == 64 || head_dim == 128) && supported_block(block_size) &&
          (dtype == PKV_BF16 || dtype == PKV_FP16);
 }
 
@@ -167,7 +169,8 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* k_pool, v
       ((uintptr_t)slot_mapping & 7u))
     return PKV_ERR_ALIGNMENT;
   const hipError_t err = pkv::launch_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping,
-                                                       num_tokens, num_kv_heads, head_dim, stream);
+                                                       num_tokens, num_kv_heads, head_dim,
+                                                       block_size, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -188,7 +191,7 @@ pkv_status copy_blocks(const pkv_pool* pool, const int32_t* src_blocks, const in
 int paged_attention_num_workgroups(int num_seqs, int num_q_heads, int num_kv_heads,
                                    int max_context_len, int block_size) {
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size, 0) ||
-      block_size != pkv::kBlock)
+      !supported_block(block_size))
     return 0;
   return default_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len);
 }
@@ -198,7 +201,7 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
                                        int num_workgroups) {
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size,
                        num_workgroups) ||
-      head_dim <= 0 || block_size != pkv::kBlock)
+      head_dim <= 0 || !supported_block(block_size))
     return (size_t)-1;
   const int grid = resolve_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len,
                                       num_workgroups);
@@ -258,6 +261,7 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
   a.head_tiles = head_tiles;
   a.max_blocks = max_blocks_per_seq;
   a.max_tokens = max_blocks_per_seq * block_size;
+  a.sub_shift = block_size == 32 ? 1 : 0;
   const hipError_t err = pkv::launch_decode(a, grid, head_dim, dtype == PKV_BF16, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -18,7 +18,7 @@ template <int D>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const unsigned short* __restrict__ key, const unsigned short* __restrict__ value,
     unsigned short* __restrict__ k_pool, unsigned short* __restrict__ v_pool,
-    const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads) {
+    const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads, int block_size) {
   constexpr int kChunks = D / 8;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long total = (long)num_tokens * num_kv_heads * kChunks;
@@ -29,9 +29,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const long i = r / num_kv_heads;
   const int64_t slot = slot_mapping[i];
   if (slot < 0) return;
-  const int64_t b = slot / kBlock;
-  const int t = (int)(slot % kBlock);
-  const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)(kBlock * D);
+  const int64_t b = slot / block_size;
+  const int tb = (int)(slot % block_size);
+  const int t = tb % kBlock;  // token within its 16-token sub-tile
+  // tile of (block, kv head), then the sub-tile holding the token
+  const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)block_size * D +
+                      (size_t)(tb / kBlock) * (kBlock * D);
   const size_t src = ((size_t)i * num_kv_heads + h) * D + 8 * c;
 
   *(u32x4*)(k_pool + tile + c * 128 + t * 8) = *(const u32x4*)(key + src);
@@ -84,7 +87,7 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, size_t layer_bytes, si
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
-                                    int head_dim, hipStream_t stream) {
+                                    int head_dim, int block_size, hipStream_t stream) {
   const long total = (long)num_tokens * num_kv_heads * (head_dim / 8);
   if (total == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((total + 255) / 256);
@@ -94,10 +97,10 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   auto* vp = (unsigned short*)v_pool;
   if (head_dim == 128) {
     hipLaunchKernelGGL(reshape_and_cache_kernel<128>, dim3(blocks), dim3(256), 0, stream, k, v, kp,
-                       vp, slot_mapping, num_tokens, num_kv_heads);
+                       vp, slot_mapping, num_tokens, num_kv_heads, block_size);
   } else {
     hipLaunchKernelGGL(reshape_and_cache_kernel<64>, dim3(blocks), dim3(256), 0, stream, k, v, kp,
-                       vp, slot_mapping, num_tokens, num_kv_heads);
+                       vp, slot_mapping, num_tokens, num_kv_heads, block_size);
   }
   return hipGetLastError();
 }

@@ -313,7 +313,8 @@ paged_decode_kernel(DecodeLaunch a) {
     next_qrow = cur.nvalid;
   }
 
-  // ---- Tile ids: lane l of window c holds the tile of this wave's position 64c + l. ----
+  // ---- Tile ids: lane l of window c holds the 16-token sub-tile of this wave's position 64c + l
+  // (its index in units of 16 * D elements of the layer's pool). ----
   const int span = r1 - r0;
   const int mw = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;  // this wave's blocks
   auto window = [&](int c) -> unsigned {
@@ -326,8 +327,11 @@ paged_decode_kernel(DecodeLaunch a) {
     const int gh = r / nb;
     const int j = r - gh * nb;
     const int g = gh / a.head_tiles;
-    return (unsigned)a.block_tables[(size_t)s * a.max_blocks + j] * (unsigned)a.num_kv_heads +
-           (unsigned)g;
+    // 16-token unit j of the stream: sub-tile j % R of physical block block_tables[s][j / R]
+    // (R = block_size / 16 sub-tiles per block, each 16 * D elements of the block's tile).
+    const unsigned b = (unsigned)a.block_tables[(size_t)s * a.max_blocks + (j >> a.sub_shift)];
+    return ((b * (unsigned)a.num_kv_heads + (unsigned)g) << a.sub_shift) +
+           (unsigned)(j & ((1 << a.sub_shift) - 1));
   };
   unsigned win_a = window(0);
   unsigned win_b = mw > 64 ? window(1) : 0u;

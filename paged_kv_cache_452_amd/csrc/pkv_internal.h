@@ -7,7 +7,8 @@
 
 namespace pkv {
 
-constexpr int kBlock = 16;          // tokens per physical block this build supports
+constexpr int kBlock = 16;          // tokens per sub-tile: the decode's unit of work (a
+                                    // physical block holds 1 or 2 sub-tiles: block size 16 or 32)
 constexpr int kMaxGroupTile = 16;   // query heads per wave (matrix-core N dimension)
 constexpr int kWaves = 4;           // wavefronts per decode workgroup
 constexpr int kMaxSeqs = 2048;      // sequences one decode launch plans for (LDS prefix sums)
@@ -30,7 +31,8 @@ struct DecodeLaunch {
   int group;            // num_q_heads / num_kv_heads
   int head_tiles;       // ceil(group / 16)
   int max_blocks;       // block table row length
-  int max_tokens;       // max_blocks * 16: context lengths are clamped to it
+  int max_tokens;       // max_blocks * block_size: context lengths are clamped to it
+  int sub_shift;        // log2(block_size / 16): sub-tiles per physical block = 1 << sub_shift
 };
 
 // Launch the decode kernel on `grid` workgroups. Returns a hipError_t.
@@ -44,6 +46,6 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, size_t layer_bytes, si
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
-                                    int head_dim, hipStream_t stream);
+                                    int head_dim, int block_size, hipStream_t stream);
 
 }  // namespace pkv

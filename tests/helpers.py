@@ -37,27 +37,28 @@ def oracle_dtype(t: torch.Tensor) -> int:
 
 
 def gpu_decode(q, k_layer, v_layer, block_tables, context_lens, scale, Hq, Hkv, max_ctx,
-               num_workgroups=0, out=None, workspace=None):
+               num_workgroups=0, out=None, workspace=None, block_size=16):
     """Run the HIP decode; a fresh zeroed workspace unless one is passed in."""
     D = q.shape[-1]
     S = q.shape[0]
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        nbytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, max_ctx, num_workgroups)
+        nbytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, block_size, max_ctx,
+                                                     num_workgroups)
         workspace = pkv.new_workspace(nbytes, q.device)
     pkv.paged_attention_decode(out, q, k_layer, v_layer, block_tables, context_lens, scale, Hq,
-                               Hkv, D, 16, max_ctx, num_workgroups, workspace)
+                               Hkv, D, block_size, max_ctx, num_workgroups, workspace)
     return out
 
 
 def oracle_decode(q, k_layer, v_layer, block_tables, context_lens, scale, Hq, Hkv, num_blocks,
-                  pairs=None, k_words=None, v_words=None):
+                  pairs=None, k_words=None, v_words=None, block_size=16):
     kw = words(k_layer) if k_words is None else k_words
     vw = words(v_layer) if v_words is None else v_words
     bt = block_tables.cpu().numpy() if isinstance(block_tables, torch.Tensor) else block_tables
     cl = context_lens.cpu().numpy() if isinstance(context_lens, torch.Tensor) else context_lens
-    return oracle.paged_decode(words(q), kw, vw, bt, cl, scale, Hq, Hkv, q.shape[-1], 16,
+    return oracle.paged_decode(words(q), kw, vw, bt, cl, scale, Hq, Hkv, q.shape[-1], block_size,
                                num_blocks, oracle_dtype(q), pairs=pairs, threads=host_threads())
 
 
@@ -78,20 +79,21 @@ def assert_close(got: torch.Tensor, ref: np.ndarray, what: str = ""):
 
 
 def poison_dead_slots_(k_layer: torch.Tensor, v_layer: torch.Tensor, tables, lens,
-                       num_kv_heads: int, head_dim: int):
+                       num_kv_heads: int, head_dim: int, block_size: int = 16):
     """Write NaN into the unwritten slots (t >= n) of every sequence's last block, locating
     them with the oracle's layout function."""
+    B = block_size
     idx = []
     for s, n in enumerate(lens):
         n = int(n)
-        if n % 16 == 0:
+        if n % B == 0:
             continue
-        b = int(tables[s][n // 16])
-        for t in range(n % 16, 16):
+        b = int(tables[s][n // B])
+        for t in range(n % B, B):
             for h in range(num_kv_heads):
                 for d in range(head_dim):
-                    idx.append((oracle.pool_index(False, b, h, t, d, num_kv_heads, 16, head_dim),
-                                oracle.pool_index(True, b, h, t, d, num_kv_heads, 16, head_dim)))
+                    idx.append((oracle.pool_index(False, b, h, t, d, num_kv_heads, B, head_dim),
+                                oracle.pool_index(True, b, h, t, d, num_kv_heads, B, head_dim)))
     if not idx:
         return
     ia = torch.tensor(idx, dtype=torch.long, device=k_layer.device)

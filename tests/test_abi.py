@@ -48,6 +48,7 @@ def test_kv_pool_bytes_matches_sizing_formula():
     # unsupported shapes and bad sizes give 0
     assert pkv.kv_pool_bytes(1, 64, 4, 96, 16, pkv.PKV_BF16) == 0
     assert pkv.kv_pool_bytes(1, 64, 4, 128, 8, pkv.PKV_BF16) == 0
+    assert pkv.kv_pool_bytes(1, 64, 4, 128, 32, pkv.PKV_BF16) == 64 * 4 * 32 * 128 * 2
     assert pkv.kv_pool_bytes(0, 64, 4, 128, 16, pkv.PKV_BF16) == 0
     assert pkv.kv_pool_bytes(1, 64, 4, 128, 16, 7) == 0
     # overflow is detected
@@ -97,7 +98,8 @@ def test_decode_argument_errors_return_before_launch():
     assert _decode(lib, hq=30, hkv=8) == INVALID            # head ratio
     assert _decode(lib, hkv=0) == INVALID
     assert _decode(lib, d=96) == UNSUPPORTED
-    assert _decode(lib, b=32) == UNSUPPORTED
+    assert _decode(lib, b=48) == UNSUPPORTED
+    assert _decode(lib, b=8) == UNSUPPORTED
     assert _decode(lib, dt=5) == UNSUPPORTED
     assert _decode(lib, q=None, ws=FAKE, wsb=1 << 30) == INVALID
     assert _decode(lib, out=FAKE + 2) == ALIGN

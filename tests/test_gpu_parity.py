@@ -113,16 +113,17 @@ def test_config4_all_80_layers_sampled():
     torch.cuda.empty_cache()
 
 
-def _random_case(Hq, Hkv, D, lens, dtype=torch.bfloat16, seed=0, extra_blocks=7):
+def _random_case(Hq, Hkv, D, lens, dtype=torch.bfloat16, seed=0, extra_blocks=7, block_size=16):
     """A small paged batch with NaN-poisoned unused blocks and dead slots."""
     lens = np.asarray(lens, np.int32)
-    spec = workloads.Spec(0, f"case Hq={Hq} Hkv={Hkv} D={D} lens={lens.tolist()}", len(lens), Hq,
-                          Hkv, D, "bf16" if dtype == torch.bfloat16 else "fp16", 1, seed=seed)
-    need = sum(-(-int(n) // 16) for n in lens)
+    spec = workloads.Spec(0, f"case Hq={Hq} Hkv={Hkv} D={D} B={block_size} lens={lens.tolist()}",
+                          len(lens), Hq, Hkv, D, "bf16" if dtype == torch.bfloat16 else "fp16", 1,
+                          seed=seed, block_size=block_size)
+    need = sum(-(-int(n) // block_size) for n in lens)
     t = workloads.make_tables(spec, lens=lens, num_blocks=max(need + extra_blocks, 1), seed=seed)
     b = workloads.make_batch(spec, device=DEV, tables=t)
     k, v = _layer(b)
-    poison_dead_slots_(k, v, t.block_tables, t.context_lens, Hkv, D)
+    poison_dead_slots_(k, v, t.block_tables, t.context_lens, Hkv, D, block_size)
     return spec, t, b
 
 
@@ -213,3 +214,36 @@ def test_max_context_fills_block_table():
     ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 8, 2,
                         t.num_blocks)
     assert_close(out, ref, "max context")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,lens,nwg", [
+    (32, 8, 128, torch.bfloat16, [1, 16, 17, 31, 32, 33, 500, 4097], 0),   # ragged sub-tiles
+    (8, 8, 64, torch.float16, [63, 64, 65, 1000], 0),
+    (32, 8, 128, torch.bfloat16, [3000, 7, 32 * 40], 200),                 # many split streams
+    (64, 2, 128, torch.bfloat16, [33, 2049], 3),
+])
+def test_block_size_32_decode(Hq, Hkv, D, dtype, lens, nwg):
+    """Block size 32: a block holds two 16-token sub-tiles; decode walks them through the table."""
+    spec, t, b = _random_case(Hq, Hkv, D, lens, dtype, seed=len(lens) + D, block_size=32)
+    k, v = _layer(b)
+    say("block size 32", spec.name, nwg)
+    out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, Hq, Hkv,
+                     int(max(lens)), nwg, block_size=32)
+    torch.cuda.synchronize()
+    ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, Hq, Hkv,
+                        t.num_blocks, block_size=32)
+    assert_close(out, ref, spec.name)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_size_32_reshape_and_cache_bit_exact(D):
+    lens = [1, 16, 17, 32, 33, 64, 90]
+    spec, t, b = _random_case(8, 4, D, lens, seed=D, block_size=32)
+    k, v = _layer(b)
+    kw, vw = words(k), words(v)
+    oracle.reshape_and_cache(kw, vw, b.new_key.cpu(), b.new_value.cpu(), t.slot_mapping, 4, D, 32,
+                             t.num_blocks)
+    say("reshape block size 32", D)
+    pkv.reshape_and_cache(b.new_key, b.new_value, k, v, b.slot_mapping, t.num_blocks, 32)
+    torch.cuda.synchronize()
+    assert np.array_equal(words(k), kw) and np.array_equal(words(v), vw)
