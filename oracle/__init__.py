@@ -55,6 +55,18 @@ def _load():
     lib.oracle_paged_decode.restype = i
     lib.oracle_reshape_and_cache.argtypes = [p, p, p, p, p, i, i, i, i, lg]
     lib.oracle_reshape_and_cache.restype = i
+    lib.oracle_e4m3_value.argtypes = [i]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_e4m3_encode.restype = i
+    lib.oracle_pool_index8.argtypes = [i, lg, i, i, i, i, i, i]
+    lib.oracle_pool_index8.restype = lg
+    f = ctypes.c_float
+    lib.oracle_paged_decode8.argtypes = [p, p, p, p, f, f, i, p, p, i, i, i, i, i, lg, i, f, p, i,
+                                         i]
+    lib.oracle_paged_decode8.restype = i
+    lib.oracle_reshape_and_cache8.argtypes = [p, p, p, p, i, f, f, p, i, i, i, i, lg]
+    lib.oracle_reshape_and_cache8.restype = i
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     _lib = lib
@@ -150,5 +162,83 @@ def reshape_and_cache(k_pool: np.ndarray, v_pool: np.ndarray, key, value, slot_m
     rc = _load().oracle_reshape_and_cache(_ptr(k_pool), _ptr(v_pool), _ptr(kw), _ptr(vw),
                                           _ptr(sm), sm.shape[0], num_kv_heads, head_dim,
                                           block_size, num_blocks)
+    if rc != 0:
+        raise ValueError("slot out of range")
+
+
+# ---- fp8 (OCP E4M3) KV pools: one fp32 scale per pool; value = e4m3_value(code) * scale ----
+
+def e4m3_value(code: int) -> float:
+    """Value of an 8-bit E4M3 code (from the format's definition)."""
+    return float(_load().oracle_e4m3_value(int(code)))
+
+
+def e4m3_encode(y: float) -> int:
+    """Nearest E4M3 code to the fp32 value y (ties to even, saturating, NaN kept)."""
+    return int(_load().oracle_e4m3_encode(ctypes.c_float(y)))
+
+
+def pool_index8(is_v: bool, block: int, kv_head: int, slot: int, dim: int, num_kv_heads: int,
+                block_size: int, head_dim: int) -> int:
+    """Byte index of (block, kv head, token slot, dim) in one layer's fp8 K or V pool."""
+    return int(_load().oracle_pool_index8(int(bool(is_v)), block, kv_head, slot, dim,
+                                          num_kv_heads, block_size, head_dim))
+
+
+def _bytes(a) -> np.ndarray:
+    if not isinstance(a, np.ndarray):
+        import torch
+        if a.dtype != torch.uint8:
+            a = a.view(torch.uint8)
+        a = a.contiguous().numpy()
+    if a.dtype != np.uint8:
+        a = a.view(np.uint8)
+    return np.ascontiguousarray(a)
+
+
+def paged_decode8(q, k_pool, v_pool, k_scale: float, v_scale: float, block_tables, context_lens,
+                  scale: float, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                  block_size: int, num_blocks: int, dtype: int, pairs=None,
+                  threads: int = 0) -> np.ndarray:
+    """fp64 decode attention over fp8 pools (q 16-bit). Returns [S][Hq][D] or [len(pairs)][D]."""
+    qw, kp, vp = _words(q), _bytes(k_pool), _bytes(v_pool)
+    bt, cl = _i32(block_tables), _i32(context_lens)
+    S = cl.shape[0]
+    max_blocks = bt.shape[1] if bt.ndim == 2 else 0
+    if pairs is None:
+        out = np.zeros((S, num_q_heads, head_dim), np.float64)
+        pp, npairs = None, 0
+    else:
+        pa = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        out = np.zeros((pa.shape[0], head_dim), np.float64)
+        pp, npairs = _ptr(pa), pa.shape[0]
+    f = ctypes.c_float
+    rc = _load().oracle_paged_decode8(_ptr(out), _ptr(qw), _ptr(kp), _ptr(vp), f(k_scale),
+                                      f(v_scale), dtype, _ptr(bt), _ptr(cl), S, num_q_heads,
+                                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks,
+                                      f(scale), pp, npairs, threads)
+    if rc != 0:
+        raise ValueError(f"oracle_paged_decode8 failed ({rc})")
+    return out
+
+
+def reshape_and_cache8(k_pool: np.ndarray, v_pool: np.ndarray, key, value, dtype: int,
+                       k_scale: float, v_scale: float, slot_mapping, num_kv_heads: int,
+                       head_dim: int, block_size: int, num_blocks: int) -> None:
+    """In-place host scatter of 16-bit new tokens, quantized to E4M3, into numpy uint8 copies of
+    one layer's fp8 pools."""
+    if k_pool.dtype != np.uint8 or v_pool.dtype != np.uint8:
+        raise TypeError("pools must be uint8 numpy arrays (modified in place)")
+    if not (k_pool.flags.c_contiguous and v_pool.flags.c_contiguous):
+        raise ValueError("pools must be contiguous")
+    kw, vw = _words(key), _words(value)
+    sm = slot_mapping
+    if not isinstance(sm, np.ndarray):
+        sm = sm.contiguous().numpy()
+    sm = np.ascontiguousarray(sm, dtype=np.int64)
+    f = ctypes.c_float
+    rc = _load().oracle_reshape_and_cache8(_ptr(k_pool), _ptr(v_pool), _ptr(kw), _ptr(vw), dtype,
+                                           f(k_scale), f(v_scale), _ptr(sm), sm.shape[0],
+                                           num_kv_heads, head_dim, block_size, num_blocks)
     if rc != 0:
         raise ValueError("slot out of range")

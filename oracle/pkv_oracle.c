@@ -30,7 +30,16 @@
  *      slot t of that block, for every kv head; negative slots are skipped.
  *
  * Pool layout: the library's documented data format — [block][kv_head][tile] with the K and V
- * tile orders described in include/pagedkv.h — re-derived here in pool_index().
+ * tile orders described in include/pagedkv.h — re-derived here in pool_index() (16-bit pools)
+ * and pool_index8() (fp8 pools).
+ *
+ * fp8 KV ("KV-Cache Management and PagedAttention", section "Planning capacity when context gets
+ * long", and "PagedAttention and KV Cache Management", section "The KV Cache Size Equation":
+ * quantizing the cache to 8 bits halves dtype_bytes). The pages name no format or scaling;
+ * the reading used here: OCP FP8 E4M3 ("e4m3fn": 1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448), one fp32 scale per pool
+ * (K and V), stored code = e4m3(fl32(x * fl32(1 / scale))) with round-to-nearest-even and
+ * saturation to the largest finite value, and value = e4m3_value(code) * scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -71,6 +80,46 @@ static double elem_value(uint16_t bits, int dtype) {
   return dtype == ORACLE_FP16 ? fp16_value(bits) : bf16_value(bits);
 }
 
+/* OCP E4M3: value of an 8-bit code, from the format's definition. */
+static double e4m3_value(uint8_t code) {
+  int sign = code >> 7;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) {
+    v = ldexp((double)m, -9); /* subnormal: (m / 8) * 2^-6 */
+  } else {
+    v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  }
+  return sign ? -v : v;
+}
+
+double oracle_e4m3_value(int code) { return e4m3_value((uint8_t)code); }
+
+/*
+ * Nearest E4M3 code to y: among the 127 non-negative finite codes, the one whose value is
+ * closest to |y| (ties to the code with an even mantissa), with y's sign; |y| beyond the largest
+ * finite value gives that value (saturation); NaN gives S.1111.111.
+ */
+static uint8_t e4m3_encode(float y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  if (isnan(y)) return (uint8_t)(sign | 0x7F);
+  double a = fabs((double)y);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double err = fabs(a - e4m3_value((uint8_t)c));
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+int oracle_e4m3_encode(float y) { return e4m3_encode(y); }
+
 /*
  * Element index of (block b, kv head h, token slot t, dim d) in one layer's K (is_v = 0) or
  * V (is_v = 1) pool. A tile of B*D elements per (block, kv head); inside it, sub-tiles of 16
@@ -97,6 +146,46 @@ static size_t pool_index(int is_v, long b, int h, int t, int d, int Hkv, int B, 
 
 long oracle_pool_index(int is_v, long b, int h, int t, int d, int Hkv, int B, int D) {
   return (long)pool_index(is_v, b, h, t, d, Hkv, B, D);
+}
+
+/*
+ * Byte index of (block b, kv head h, token slot t, dim d) in one layer's fp8 K or V pool. Same
+ * tiles and 16-token sub-tiles as pool_index (one byte per element); inside a sub-tile, K is
+ * ordered [d/64][(d/8)%4][token][(d/32)%2][d%8] and V [d/64][token/4][d%16][(d/16)%4][token%4].
+ */
+static size_t pool_index8(int is_v, long b, int h, int t, int d, int Hkv, int B, int D) {
+  size_t tile = ((size_t)b * (size_t)Hkv + (size_t)h) * (size_t)B * (size_t)D;
+  int sub = t / 16;
+  int u = t % 16;
+  size_t within;
+  if (!is_v) {
+    within = (size_t)(d / 64) * 1024 + (size_t)(16 * ((d / 8) % 4) + u) * 16 +
+             (size_t)((d / 32) % 2) * 8 + (size_t)(d % 8);
+  } else {
+    within = (size_t)(d / 64) * 1024 + (size_t)((u / 4) * 16 + d % 16) * 16 +
+             (size_t)((d / 16) % 4) * 4 + (size_t)(u % 4);
+  }
+  return tile + (size_t)sub * 16 * (size_t)D + within;
+}
+
+long oracle_pool_index8(int is_v, long b, int h, int t, int d, int Hkv, int B, int D) {
+  return (long)pool_index8(is_v, b, h, t, d, Hkv, B, D);
+}
+
+/* oracle_gather for fp8 pools: values are e4m3_value(code) * scale. */
+static int gather8(double* K_c, double* V_c, const uint8_t* k_pool, const uint8_t* v_pool,
+                   double k_scale, double v_scale, const int32_t* table, int n, int g, int Hkv,
+                   int D, int B, long num_blocks) {
+  for (int t = 0; t < n; ++t) {
+    long b = table[t / B];
+    int slot = t % B;
+    if (b < 0 || b >= num_blocks) return -1;
+    for (int d = 0; d < D; ++d) {
+      K_c[(size_t)t * D + d] = e4m3_value(k_pool[pool_index8(0, b, g, slot, d, Hkv, B, D)]) * k_scale;
+      V_c[(size_t)t * D + d] = e4m3_value(v_pool[pool_index8(1, b, g, slot, d, Hkv, B, D)]) * v_scale;
+    }
+  }
+  return 0;
 }
 
 /*
@@ -194,6 +283,91 @@ int oracle_paged_decode(double* out, const uint16_t* q, const uint16_t* k_pool,
     free(V_c);
   }
   return status;
+}
+
+/*
+ * oracle_paged_decode over fp8 pools (scales k_scale, v_scale); q in bf16/fp16 (dtype).
+ */
+int oracle_paged_decode8(double* out, const uint16_t* q, const uint8_t* k_pool,
+                         const uint8_t* v_pool, float k_scale, float v_scale, int dtype,
+                         const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                         int Hq, int Hkv, int D, int B, long num_blocks, int max_blocks,
+                         float scale, const int32_t* pairs, int npairs, int nthreads) {
+  if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0 || num_seqs < 0) return -2;
+  int group = Hq / Hkv;
+  long count = pairs ? (long)npairs : (long)num_seqs * Hq;
+  int status = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long i = 0; i < count; ++i) {
+    int s = pairs ? pairs[2 * i] : (int)(i / Hq);
+    int h = pairs ? pairs[2 * i + 1] : (int)(i % Hq);
+    double* row = out + (size_t)i * D;
+    if (s < 0 || s >= num_seqs || h < 0 || h >= Hq) {
+#pragma omp atomic write
+      status = -2;
+      continue;
+    }
+    int n = context_lens[s];
+    if (n < 0 || n > max_blocks * B) {
+#pragma omp atomic write
+      status = -2;
+      continue;
+    }
+    int g = h / group;
+    double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+    double* K_c = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+    double* V_c = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+    for (int d = 0; d < D; ++d) qd[d] = elem_value(q[((size_t)s * Hq + h) * D + d], dtype);
+    if (gather8(K_c, V_c, k_pool, v_pool, (double)k_scale, (double)v_scale,
+                block_tables + (size_t)s * max_blocks, n, g, Hkv, D, B, num_blocks) != 0) {
+#pragma omp atomic write
+      status = -1;
+    } else {
+      dense_attention(row, qd, K_c, V_c, n, D, (double)scale);
+    }
+    free(qd);
+    free(K_c);
+    free(V_c);
+  }
+  return status;
+}
+
+/*
+ * Host scatter into copies of one layer's fp8 pools: key/value are [T][Hkv][D] 16-bit words of
+ * type dtype; the stored code is e4m3(fl32(x * fl32(1 / scale))). Returns 0, or -1 for a slot
+ * beyond the pool.
+ */
+int oracle_reshape_and_cache8(uint8_t* k_pool, uint8_t* v_pool, const uint16_t* key,
+                              const uint16_t* value, int dtype, float k_scale, float v_scale,
+                              const int64_t* slot_mapping, int T, int Hkv, int D, int B,
+                              long num_blocks) {
+  volatile float one = 1.0f;  /* fp32 arithmetic, as stated above */
+  float k_inv = one / k_scale;
+  float v_inv = one / v_scale;
+  for (int i = 0; i < T; ++i) {
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    if (slot >= (int64_t)num_blocks * B) return -1;
+    long b = (long)(slot / B);
+    int t = (int)(slot % B);
+    for (int h = 0; h < Hkv; ++h) {
+      for (int d = 0; d < D; ++d) {
+        size_t src = ((size_t)i * Hkv + h) * D + d;
+        float kx = (float)elem_value(key[src], dtype);
+        float vx = (float)elem_value(value[src], dtype);
+        float ky = kx * k_inv;
+        float vy = vx * v_inv;
+        k_pool[pool_index8(0, b, h, t, d, Hkv, B, D)] = e4m3_encode(ky);
+        v_pool[pool_index8(1, b, h, t, d, Hkv, B, D)] = e4m3_encode(vy);
+      }
+    }
+  }
+  return 0;
 }
 
 /*

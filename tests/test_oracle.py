@@ -354,3 +354,139 @@ def test_reshape_skips_negative_slots_and_rejects_out_of_range():
     assert np.count_nonzero(kp) == np.count_nonzero(key[1])
     with pytest.raises(ValueError):
         oracle.reshape_and_cache(kp, vp, key, key, np.array([NB * B, 0], np.int64), Hkv, D, B, NB)
+
+
+# ---- fp8 (OCP E4M3) KV pools -------------------------------------------------------------
+
+def test_e4m3_decoding_exhaustive_against_torch():
+    """All 256 codes: the oracle's definition-based value equals torch's float8_e4m3fn."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    want = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6 and oracle.e4m3_value(0x38) == 1.0
+
+
+def test_e4m3_encoding_matches_torch_in_range():
+    """Round to nearest even against torch's float8_e4m3fn cast wherever the two readings agree
+    (|y| < 464, below the first value torch sends to NaN): every bf16 bit pattern in range, plus
+    random fp32 values."""
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    ys = bits.to(torch.float32)
+    rng = np.random.default_rng(5)
+    extra = torch.from_numpy(np.concatenate([
+        rng.standard_normal(20000) * s for s in (1e-3, 0.05, 1.0, 30.0, 200.0)]).astype(np.float32))
+    ys = torch.cat([ys, extra])
+    ys = ys[torch.isfinite(ys) & (ys.abs() < 464.0)]
+    want = ys.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(float(y)) for y in ys.numpy()], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_encoding_saturates_and_keeps_nan_and_sign():
+    """The reading for values the pages leave open: beyond the largest finite value the code
+    saturates to +-448; NaN stays NaN with its sign; -0 keeps its sign."""
+    for y, c in [(464.0, 0x7E), (480.0, 0x7E), (1e30, 0x7E), (float("inf"), 0x7E),
+                 (-500.0, 0xFE), (float("nan"), 0x7F), (-0.0, 0x80), (-1e-9, 0x80)]:
+        assert oracle.e4m3_encode(y) == c, (y, c)
+
+
+def test_e4m3_round_trip_error_bound():
+    """Every finite code round-trips exactly, and quantization error is at most half a step."""
+    for c in list(range(0x7F)) + list(range(0x80, 0xFF)):
+        assert oracle.e4m3_encode(oracle.e4m3_value(c)) == c
+    rng = np.random.default_rng(6)
+    for y in rng.standard_normal(2000).astype(np.float32) * 10:
+        v = oracle.e4m3_value(oracle.e4m3_encode(float(y)))
+        e = max(math.floor(math.log2(abs(y))), -6) if y != 0 else -6
+        assert abs(v - float(y)) <= 2.0 ** (e - 3) / 2 + 1e-30
+
+
+def test_fp8_pool_layout_worked_offsets_and_bijection():
+    g = _load("tile_layout_fp8.json")
+    D, B = g["head_dim"], g["block_size"]
+    for t, d, off in g["k"]:
+        assert oracle.pool_index8(False, 0, 0, t, d, 1, B, D) == off
+    for t, d, off in g["v"]:
+        assert oracle.pool_index8(True, 0, 0, t, d, 1, B, D) == off
+    for D, B in [(64, 16), (128, 16), (128, 32), (64, 32)]:
+        for is_v in (False, True):
+            seen = sorted(oracle.pool_index8(is_v, 2, 1, t, d, 3, B, D)
+                          for t in range(B) for d in range(D))
+            base = (2 * 3 + 1) * B * D
+            assert seen == list(range(base, base + B * D))
+
+
+def test_fp8_decode_equals_16bit_decode_on_exactly_representable_values():
+    """With power-of-two scales every dequantized value is exactly a bf16 value: decode over fp8
+    pools must equal decode over 16-bit pools holding those values (an independent path)."""
+    rng = np.random.default_rng(8)
+    Hq, Hkv, D, B, NB = 8, 2, 64, 16, 16
+    lens = np.array([1, 17, 40, 100], np.int32)   # 13 blocks
+    tables = np.full((4, 8), -1, np.int32)
+    perm = rng.permutation(NB)
+    p = 0
+    for s, n in enumerate(lens):
+        k = -(-int(n) // B)
+        tables[s, :k] = perm[p:p + k]
+        p += k
+    kb = rng.integers(0, 256, size=NB * Hkv * B * D).astype(np.uint8)
+    vb = rng.integers(0, 256, size=NB * Hkv * B * D).astype(np.uint8)
+    kb[(kb & 0x7F) == 0x7F] = 0x10   # no NaN codes
+    vb[(vb & 0x7F) == 0x7F] = 0x11
+    ks, vs = 0.25, 4.0
+    kw = np.zeros(NB * Hkv * B * D, np.uint16)
+    vw = np.zeros(NB * Hkv * B * D, np.uint16)
+    for b in range(NB):
+        for h in range(Hkv):
+            for t in range(B):
+                for d in range(D):
+                    i8k = oracle.pool_index8(False, b, h, t, d, Hkv, B, D)
+                    i8v = oracle.pool_index8(True, b, h, t, d, Hkv, B, D)
+                    kval = torch.tensor(oracle.e4m3_value(kb[i8k]) * ks, dtype=torch.float64)
+                    vval = torch.tensor(oracle.e4m3_value(vb[i8v]) * vs, dtype=torch.float64)
+                    kw[oracle.pool_index(False, b, h, t, d, Hkv, B, D)] = kval.to(
+                        torch.bfloat16).view(torch.int16).item() & 0xFFFF
+                    vw[oracle.pool_index(True, b, h, t, d, Hkv, B, D)] = vval.to(
+                        torch.bfloat16).view(torch.int16).item() & 0xFFFF
+    q = torch.randn(4, Hq, D, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    got = oracle.paged_decode8(q, kb, vb, ks, vs, tables, lens, 0.125, Hq, Hkv, D, B, NB,
+                               oracle.BF16)
+    want = oracle.paged_decode(q, kw, vw, tables, lens, 0.125, Hq, Hkv, D, B, NB, oracle.BF16)
+    assert np.array_equal(got, want)
+
+
+def test_fp8_scatter_quantizes_each_element():
+    """reshape_and_cache8 stores e4m3(fl32(x * fl32(1/scale))) at pool_index8 and nothing else."""
+    rng = np.random.default_rng(9)
+    Hkv, D, B, NB = 2, 64, 16, 4
+    T = 3
+    key = torch.randn(T, Hkv, D, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    val = torch.randn(T, Hkv, D, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    kp = np.full(NB * Hkv * B * D, 0xAA, np.uint8)
+    vp = np.full(NB * Hkv * B * D, 0xAA, np.uint8)
+    slots = np.array([5, -1, 3 * 16 + 15], np.int64)
+    ks, vs = 0.3, 0.07
+    oracle.reshape_and_cache8(kp, vp, key, val, oracle.BF16, ks, vs, slots, Hkv, D, B, NB)
+    kinv = np.float32(1.0) / np.float32(ks)
+    vinv = np.float32(1.0) / np.float32(vs)
+    touched = set()
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        b, t = divmod(int(slot), B)
+        for h in range(Hkv):
+            for d in range(D):
+                kx = np.float32(key[i, h, d].float().item()) * kinv
+                vx = np.float32(val[i, h, d].float().item()) * vinv
+                ik = oracle.pool_index8(False, b, h, t, d, Hkv, B, D)
+                iv = oracle.pool_index8(True, b, h, t, d, Hkv, B, D)
+                assert kp[ik] == oracle.e4m3_encode(float(kx))
+                assert vp[iv] == oracle.e4m3_encode(float(vx))
+                touched.add(ik)
+    untouched = np.ones(kp.shape[0], bool)
+    untouched[list(touched)] = False
+    assert np.all(kp[untouched] == 0xAA)
