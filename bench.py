@@ -25,10 +25,12 @@ DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_452_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
-def algorithmic_bytes(lens, num_q_heads, num_kv_heads, head_dim, elem=2, block=16):
+def algorithmic_bytes(lens, num_q_heads, num_kv_heads, head_dim, elem=2, block=16, kv_elem=None):
     """Bytes one decode launch must move: every cached K and V row of every sequence once per kv
-    head, q in, out back, the used block-table entries and the context lengths."""
-    kv = sum(int(n) for n in lens) * num_kv_heads * head_dim * elem * 2
+    head, q in, out back, the used block-table entries and the context lengths. elem: bytes of a
+    q/out element; kv_elem: bytes of a pool element (default elem; 1 for fp8 pools)."""
+    kv_elem = elem if kv_elem is None else kv_elem
+    kv = sum(int(n) for n in lens) * num_kv_heads * head_dim * kv_elem * 2
     qo = len(lens) * num_q_heads * head_dim * elem * 2
     tables = sum(-(-int(n) // block) for n in lens) * 4
     return kv + qo + tables + 4 * len(lens)
@@ -52,28 +54,40 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(batch, spec, layers, budget_s=15.0):
-    """The fp64 oracle on the host cores over whole layers of the same batch (bounded)."""
+def cpu_baseline(batch, spec, layers, budget_s=15.0, kv_scales=None):
+    """The fp64 oracle on the host cores over whole layers of the same batch (bounded).
+    kv_scales: (k_scale, v_scale) when the pools hold fp8 codes."""
     import numpy as np
     import torch
     import oracle
 
     threads = len(os.sched_getaffinity(0))
     t = batch.tables
+    qdt = oracle.BF16 if spec.dtype == "bf16" else oracle.FP16
     per_layer = algorithmic_bytes(t.context_lens, spec.num_q_heads, spec.num_kv_heads,
-                                  spec.head_dim)
+                                  spec.head_dim, block=spec.block_size,
+                                  kv_elem=1 if kv_scales else 2)
     done_bytes, cpu_s, d2h_s, n_layers = 0, 0.0, 0.0, 0
     q = batch.q.cpu()
     for L in layers:
         t0 = time.perf_counter()
-        kw = batch.k_pool[L].view(torch.int16).cpu().numpy().view(np.uint16)
-        vw = batch.v_pool[L].view(torch.int16).cpu().numpy().view(np.uint16)
+        if kv_scales:
+            kw = batch.k_pool[L].cpu().numpy()
+            vw = batch.v_pool[L].cpu().numpy()
+        else:
+            kw = batch.k_pool[L].view(torch.int16).cpu().numpy().view(np.uint16)
+            vw = batch.v_pool[L].view(torch.int16).cpu().numpy().view(np.uint16)
         d2h_s += time.perf_counter() - t0
         t0 = time.perf_counter()
-        oracle.paged_decode(q, kw, vw, t.block_tables, t.context_lens, spec.scale,
-                            spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size,
-                            t.num_blocks,
-                            oracle.BF16, threads=threads)
+        if kv_scales:
+            oracle.paged_decode8(q, kw, vw, kv_scales[0], kv_scales[1], t.block_tables,
+                                 t.context_lens, spec.scale, spec.num_q_heads, spec.num_kv_heads,
+                                 spec.head_dim, spec.block_size, t.num_blocks, qdt,
+                                 threads=threads)
+        else:
+            oracle.paged_decode(q, kw, vw, t.block_tables, t.context_lens, spec.scale,
+                                spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                                spec.block_size, t.num_blocks, qdt, threads=threads)
         cpu_s += time.perf_counter() - t0
         done_bytes += per_layer
         n_layers += 1
@@ -176,6 +190,9 @@ def main() -> int:
                     help="layers in the pool (default: the workload's own; more layers of fresh "
                          "data keep a small single-layer workload from being served out of the "
                          "256 MB last-level cache between launches)")
+    ap.add_argument("--kv-dtype", choices=["model", "fp8"], default="model",
+                    help="pool element type: the model's 16-bit type (default) or E4M3 codes "
+                         "with one scale per pool")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel", choices=["decode", "copy_blocks"], default="decode",
                     help="decode (the hot path, default) or copy_blocks (copy-on-write copies)")
@@ -204,7 +221,12 @@ def main() -> int:
         spec = dataclasses.replace(spec, block_size=args.block_size)
     B = spec.block_size
     t = workloads.make_tables(spec)
-    batch = workloads.make_batch(spec, device=dev, tables=t)
+    fp8 = args.kv_dtype == "fp8"
+    ks, vs = 0.05, 0.05   # per-pool scales of the fp8 path (values do not change its cost)
+    if fp8:
+        batch = workloads.make_batch_fp8(spec, device=dev, tables=t)
+    else:
+        batch = workloads.make_batch(spec, device=dev, tables=t)
     S, Hq, Hkv, D, L = (spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                         spec.num_layers)
     max_ctx = int(t.context_lens.max())
@@ -215,19 +237,32 @@ def main() -> int:
     layers = [(batch.k_pool[i], batch.v_pool[i]) for i in range(L)]
     stream = torch.cuda.current_stream()
 
-    def step():
-        for i, (k, v) in enumerate(layers):
+    def cache(k, v):
+        if fp8:
+            pkv.reshape_and_cache_fp8(batch.new_key, batch.new_value, k, v, batch.slot_mapping,
+                                      t.num_blocks, ks, vs, B, stream)
+        else:
             pkv.reshape_and_cache(batch.new_key, batch.new_value, k, v, batch.slot_mapping,
                                   t.num_blocks, B, stream)
+
+    def decode(i, k, v):
+        if fp8:
+            pkv.paged_attention_decode_fp8(outs[i], batch.q, k, v, batch.block_tables,
+                                           batch.context_lens, spec.scale, ks, vs, Hq, Hkv, D, B,
+                                           max_ctx, nwg, ws, stream)
+        else:
             pkv.paged_attention_decode(outs[i], batch.q, k, v, batch.block_tables,
                                        batch.context_lens, spec.scale, Hq, Hkv, D, B, max_ctx,
                                        nwg, ws, stream)
 
+    def step():
+        for i, (k, v) in enumerate(layers):
+            cache(k, v)
+            decode(i, k, v)
+
     def sweep_decode():
         for i, (k, v) in enumerate(layers):
-            pkv.paged_attention_decode(outs[i], batch.q, k, v, batch.block_tables,
-                                       batch.context_lens, spec.scale, Hq, Hkv, D, B, max_ctx,
-                                       nwg, ws, stream)
+            decode(i, k, v)
 
     def timed(fn, reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -250,11 +285,11 @@ def main() -> int:
     ms_total = timed(step, args.steps)
     ms_step = ms_total / args.steps
 
-    per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B)
+    per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=1 if fp8 else 2)
     value = per_launch * L / (ms_step * 1e-3) / 1e9
     achieved = per_launch / (avg_decode_ms * 1e-3) / 1e9
     workload = ((spec.name if args.layers <= 0 else f"{spec.name}, {L} layers") +
-                ("" if B == 16 else f", block size {B}"))
+                ("" if B == 16 else f", block size {B}") + (", fp8 E4M3 KV" if fp8 else ""))
     traffic = measured_traffic(workload)
     grid = nwg or pkv.paged_attention_num_workgroups(S, Hq, Hkv, max_ctx, B)
     rec = {
@@ -274,6 +309,7 @@ def main() -> int:
                    args.config == 4 else "seeded", "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": B, "num_layers": L,
                    "num_blocks_per_layer": t.num_blocks, "decode_workgroups": grid,
+                   "kv_dtype": "fp8 e4m3, one scale per pool" if fp8 else spec.dtype,
                    "step": "per layer: reshape_and_cache of the step's new tokens + "
                            "paged_attention_decode"},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -290,7 +326,8 @@ def main() -> int:
                                "streams merged in it)"},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(batch, spec, range(L))
+        rec["cpu_baseline"] = cpu_baseline(batch, spec, range(L), kv_scales=(ks, vs) if fp8
+                                           else None)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -65,6 +65,17 @@
  * 16 bytes are already the operand of one gfx950 matrix-core instruction.
  *
  * A slot is `physical_block * block_size + t` (token slot t of that block).
+ *
+ * fp8 pools (PKV_FP8_E4M3) use the same [layer][block][kv_head][tile] order and 16-token
+ * sub-tiles, one byte per element, with these orders inside a sub-tile (byte offsets):
+ *   K8 tile: k8_off(u, d) = (d / 64) * 1024 + (16 * ((d / 8) % 4) + u) * 16 + ((d / 32) % 2) * 8
+ *                           + d % 8
+ *   V8 tile: v8_off(u, d) = (d / 64) * 1024 + ((u / 4) * 16 + d % 16) * 16 + ((d / 16) % 4) * 4
+ *                           + u % 4
+ * Worked examples (D = 128, B = 16): K8 (t=1,d=0) -> 16; K8 (t=0,d=8) -> 256; K8 (t=0,d=32) -> 8;
+ * K8 (t=5,d=37) -> 93; V8 (t=0,d=1) -> 16; V8 (t=0,d=16) -> 4; V8 (t=5,d=37) -> 345.
+ * Each lane's 16 bytes are again one contiguous piece of a 1 KiB load that expands, code by
+ * code, into its matrix-core operands.
  * ---------------------------------------------------------------------------------------------
  */
 #ifndef PAGEDKV_H_
@@ -88,14 +99,17 @@ typedef enum {
   PKV_ERR_NO_BLOCKS = -6    /* the block manager's free list cannot supply the blocks needed */
 } pkv_status;
 
-typedef enum { PKV_BF16 = 0, PKV_FP16 = 1 } pkv_dtype;
+/* Element types. q, key, value and out are bf16 or fp16. Pools are bf16 or fp16 (the same type as
+ * q), or E4M3 codes (PKV_FP8_E4M3, see reshape_and_cache_fp8 / paged_attention_decode_fp8). */
+typedef enum { PKV_BF16 = 0, PKV_FP16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
 /* Opaque host-side description of one K pool and one V pool holding every layer. */
 typedef struct pkv_pool pkv_pool;
 
 /*
  * Bytes of ONE of the two pools (K or V) for all layers:
- *   num_layers * num_blocks * num_kv_heads * block_size * head_dim * 2.
+ *   num_layers * num_blocks * num_kv_heads * block_size * head_dim * element bytes
+ * (2 for bf16/fp16, 1 for PKV_FP8_E4M3).
  * This is the per-token KV size of the sizing formula ("KV-Cache Management and PagedAttention",
  * section "Why the cache exists, and why it's so hungry"; "PagedAttention and KV Cache
  * Management", section "The KV Cache Size Equation"), halved because K and V are separate pools,
@@ -132,13 +146,33 @@ void kv_pool_destroy(pkv_pool* pool);
  * Operates During Generation").
  *   key, value    device, [num_tokens][num_kv_heads][head_dim], contiguous, 16-byte aligned.
  *   k_pool,v_pool device, ONE layer's sub-pool (kv_pool_layer), 16-byte aligned.
- *   slot_mapping  device int64 [num_tokens]; slots must be < num_blocks*block_size and distinct.
+ *   slot_mapping  device int64 [num_tokens]; distinct slots. A slot >= num_blocks*block_size is
+ *                 skipped like a negative one (nothing is written outside the sub-pool).
  * num_tokens == 0 is a no-op returning PKV_OK.
  */
 pkv_status reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
                              const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                              int head_dim, int block_size, int num_blocks, pkv_dtype dtype,
                              hipStream_t stream);
+
+/*
+ * reshape_and_cache into fp8 pools: for every token i with slot_mapping[i] >= 0, kv head h and
+ * dim d, the K code at (slot / block_size, h, slot % block_size, d) becomes
+ *     e4m3(fl32(key[i][h][d] * fl32(1 / k_scale)))      (V likewise with v_scale),
+ * where e4m3 rounds to the nearest OCP E4M3 value (ties to even), saturates at +-448, and keeps
+ * NaN and the sign of zero. Quantizing the cache to 8 bits halves its bytes ("KV-Cache
+ * Management and PagedAttention", section "Planning capacity when context gets long"; "PagedAttention
+ * and KV Cache Management", section "The KV Cache Size Equation"); the format and the per-pool
+ * scale are this library's choice.
+ *   key, value    device, [num_tokens][num_kv_heads][head_dim] of src_dtype (bf16 or fp16).
+ *   k_pool,v_pool device, ONE layer's fp8 sub-pool (1 byte per element, layout above).
+ *   k_scale, v_scale  finite, > 0.
+ * Otherwise as reshape_and_cache.
+ */
+pkv_status reshape_and_cache_fp8(const void* key, const void* value, void* k_pool, void* v_pool,
+                                 const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                 int head_dim, int block_size, int num_blocks, pkv_dtype src_dtype,
+                                 float k_scale, float v_scale, hipStream_t stream);
 
 /*
  * Workgroups paged_attention_decode launches when it is passed num_workgroups == 0: enough to fill
@@ -267,6 +301,23 @@ pkv_status kv_block_manager_release(pkv_block_manager* bm, int64_t seq_id);
 pkv_status kv_block_manager_tables(const pkv_block_manager* bm, const int64_t* seq_ids,
                                    int num_seqs, int max_blocks_per_seq, int32_t* block_tables,
                                    int32_t* context_lens);
+
+/*
+ * paged_attention_decode over fp8 pools: as paged_attention_decode, with the key and value of a
+ * slot taken as e4m3_value(code) * k_scale and e4m3_value(code) * v_scale. q and out are dtype
+ * (bf16 or fp16); the pools hold E4M3 codes (PKV_FP8_E4M3 layout above). Accumulation is fp32;
+ * the codes are widened exactly to dtype for the matrix cores, k_scale is applied to the scores
+ * and v_scale to the normalised output. Workspace and errors as paged_attention_decode;
+ * k_scale, v_scale must be finite and > 0.
+ */
+pkv_status paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_tables,
+                                      const int32_t* context_lens, float scale, float k_scale,
+                                      float v_scale, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_seqs,
+                                      int max_blocks_per_seq, int max_context_len,
+                                      int num_workgroups, pkv_dtype dtype, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(pkv_status status);

@@ -17,10 +17,12 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_BF16 = 0
 PKV_FP16 = 1
+PKV_FP8_E4M3 = 2
 
 EXPORTED = ("kv_pool_bytes", "kv_pool_create", "kv_pool_layer", "kv_pool_destroy",
             "reshape_and_cache", "paged_attention_num_workgroups",
             "paged_attention_workspace_bytes", "paged_attention_decode", "copy_blocks",
+            "reshape_and_cache_fp8", "paged_attention_decode_fp8",
             "kv_block_manager_create", "kv_block_manager_destroy", "kv_block_manager_num_free",
             "kv_block_manager_allocate", "kv_block_manager_fork", "kv_block_manager_append",
             "kv_block_manager_release", "kv_block_manager_tables", "pkv_status_string")
@@ -66,6 +68,11 @@ def load_library(build_if_missing: bool = True):
     lib.paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, i,
                                            vp, sz, vp]
     lib.paged_attention_decode.restype = i
+    lib.reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, vp]
+    lib.reshape_and_cache_fp8.restype = i
+    lib.paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f, f, f, i, i, i, i, i, i,
+                                               i, i, i, vp, sz, vp]
+    lib.paged_attention_decode_fp8.restype = i
     lib.copy_blocks.argtypes = [vp, vp, vp, i, vp]
     lib.copy_blocks.restype = i
     i64 = ctypes.c_int64
@@ -236,6 +243,36 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
         float(scale), num_q_heads, num_kv_heads, head_dim, block_size, S, max_blocks,
         max_context_len, num_workgroups, _dtype_code(q), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def reshape_and_cache_fp8(key, value, k_pool, v_pool, slot_mapping, num_blocks: int,
+                          k_scale: float, v_scale: float, block_size: int = 16,
+                          stream=None) -> None:
+    """Quantize key/value [T][Hkv][D] (bf16/fp16) to E4M3 and scatter them into one layer's fp8
+    pools (uint8 tensors or device addresses) at the slots named by slot_mapping."""
+    _require_cuda(key, value, k_pool, v_pool, slot_mapping)
+    T, Hkv, D = key.shape
+    _check("reshape_and_cache_fp8", load_library().reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping), T, Hkv, D,
+        block_size, num_blocks, _dtype_code(key), float(k_scale), float(v_scale),
+        _stream(stream)))
+
+
+def paged_attention_decode_fp8(out, q, k_pool, v_pool, block_tables, context_lens, scale: float,
+                               k_scale: float, v_scale: float, num_q_heads: int,
+                               num_kv_heads: int, head_dim: int, block_size: int,
+                               max_context_len: int, num_workgroups: int = 0, workspace=None,
+                               stream=None) -> None:
+    """paged_attention_decode over fp8 (E4M3) pools with per-pool scales."""
+    _require_cuda(out, q, k_pool, v_pool, block_tables, context_lens, workspace)
+    S = q.shape[0]
+    max_blocks = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attention_decode_fp8", load_library().paged_attention_decode_fp8(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+        float(scale), float(k_scale), float(v_scale), num_q_heads, num_kv_heads, head_dim,
+        block_size, S, max_blocks, max_context_len, num_workgroups, _dtype_code(q),
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def copy_blocks(pool: "KVPool", src_blocks, dst_blocks, stream=None) -> None:

@@ -31,6 +31,15 @@ bool supported_shape(int head_dim, int block_size, pkv_dtype dtype) {
          (dtype == PKV_BF16 || dtype == PKV_FP16);
 }
 
+// Pools may also hold E4M3 codes; q, key, value and out are always 16-bit.
+bool supported_pool(int head_dim, int block_size, pkv_dtype dtype) {
+  return supported_shape(head_dim, block_size, dtype == PKV_FP8_E4M3 ? PKV_BF16 : dtype);
+}
+
+size_t elem_bytes(pkv_dtype dtype) { return dtype == PKV_FP8_E4M3 ? 1 : 2; }
+
+bool valid_scale(float s) { return isfinite(s) && s > 0.f; }
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // a * b with overflow detection (all operands non-negative).
@@ -110,8 +119,8 @@ extern "C" {
 size_t kv_pool_bytes(int num_layers, int num_blocks, int num_kv_heads, int head_dim,
                      int block_size, pkv_dtype dtype) {
   if (num_layers <= 0 || num_blocks <= 0 || num_kv_heads <= 0) return 0;
-  if (!supported_shape(head_dim, block_size, dtype)) return 0;
-  size_t r = 2;
+  if (!supported_pool(head_dim, block_size, dtype)) return 0;
+  size_t r = elem_bytes(dtype);
   const size_t f[5] = {(size_t)num_layers, (size_t)num_blocks, (size_t)num_kv_heads,
                        (size_t)block_size, (size_t)head_dim};
   for (size_t x : f) {
@@ -127,7 +136,7 @@ pkv_status kv_pool_create(pkv_pool** out, void* k_base, void* v_base, size_t byt
   *out = nullptr;
   if (k_base == nullptr || v_base == nullptr) return PKV_ERR_INVALID_ARG;
   if (num_layers <= 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
-  if (!supported_shape(head_dim, block_size, dtype)) return PKV_ERR_UNSUPPORTED;
+  if (!supported_pool(head_dim, block_size, dtype)) return PKV_ERR_UNSUPPORTED;
   if (((uintptr_t)k_base & 255u) || ((uintptr_t)v_base & 255u)) return PKV_ERR_ALIGNMENT;
   const size_t need = kv_pool_bytes(num_layers, num_blocks, num_kv_heads, head_dim, block_size,
                                     dtype);
@@ -170,7 +179,26 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* k_pool, v
     return PKV_ERR_ALIGNMENT;
   const hipError_t err = pkv::launch_reshape_and_cache(key, value, k_pool, v_pool, slot_mapping,
                                                        num_tokens, num_kv_heads, head_dim,
-                                                       block_size, stream);
+                                                       block_size, num_blocks, stream);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status reshape_and_cache_fp8(const void* key, const void* value, void* k_pool, void* v_pool,
+                                 const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                 int head_dim, int block_size, int num_blocks, pkv_dtype src_dtype,
+                                 float k_scale, float v_scale, hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PKV_ERR_INVALID_ARG;
+  if (!supported_shape(head_dim, block_size, src_dtype)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      ((uintptr_t)slot_mapping & 7u))
+    return PKV_ERR_ALIGNMENT;
+  const float one = 1.0f;
+  const hipError_t err = pkv::launch_reshape_and_cache_fp8(
+      key, value, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
+      num_blocks, src_dtype == PKV_BF16, one / k_scale, one / v_scale, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -181,7 +209,8 @@ pkv_status copy_blocks(const pkv_pool* pool, const int32_t* src_blocks, const in
   if (src_blocks == nullptr || dst_blocks == nullptr) return PKV_ERR_INVALID_ARG;
   if (((uintptr_t)src_blocks & 3u) || ((uintptr_t)dst_blocks & 3u)) return PKV_ERR_ALIGNMENT;
   if (pool->num_layers > 32767) return PKV_ERR_UNSUPPORTED;
-  const size_t block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim * 2;
+  const size_t block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim *
+                             elem_bytes(pool->dtype);
   const hipError_t err = pkv::launch_copy_blocks(pool->k, pool->v, pool->layer_bytes, block_bytes,
                                                  pool->num_layers, src_blocks, dst_blocks,
                                                  num_copies, stream);
@@ -208,15 +237,21 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
   return workspace_bytes_for(grid, head_dim);
 }
 
-pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
-                                  const int32_t* block_tables, const int32_t* context_lens,
-                                  float scale, int num_q_heads, int num_kv_heads, int head_dim,
-                                  int block_size, int num_seqs, int max_blocks_per_seq,
-                                  int max_context_len, int num_workgroups, pkv_dtype dtype,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+pkv_status decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* context_lens, float scale,
+                       bool kv_fp8, float k_scale, float v_scale, int num_q_heads,
+                       int num_kv_heads, int head_dim, int block_size, int num_seqs,
+                       int max_blocks_per_seq, int max_context_len, int num_workgroups,
+                       pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
   if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size,
                        num_workgroups) ||
-      max_blocks_per_seq < 0 || !isfinite(scale))
+      max_blocks_per_seq < 0 || !isfinite(scale) || !valid_scale(k_scale) ||
+      !valid_scale(v_scale))
     return PKV_ERR_INVALID_ARG;
   if (!supported_shape(head_dim, block_size, dtype)) return PKV_ERR_UNSUPPORTED;
   if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PKV_ERR_INVALID_ARG;
@@ -226,7 +261,8 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
   const int head_tiles = (group + pkv::kMaxGroupTile - 1) / pkv::kMaxGroupTile;
   // Flattened block positions and token counts are 32-bit on the device.
   if (max_blocks_per_seq > 2147483647 / block_size) return PKV_ERR_UNSUPPORTED;
-  if ((long double)num_seqs * max_blocks_per_seq * num_kv_heads * head_tiles >= 2147483647.0L)
+  if ((long double)num_seqs * max_blocks_per_seq * (block_size / pkv::kBlock) * num_kv_heads *
+          head_tiles >= 2147483647.0L)
     return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
@@ -253,7 +289,8 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
   a.counters = need > 0 ? (unsigned*)(ws + (workspace_bytes & ~(size_t)3) -
                                       (size_t)grid * sizeof(unsigned))
                         : nullptr;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale * k_scale * 1.4426950408889634f;
+  a.v_scale = v_scale;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -262,8 +299,39 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
   a.max_blocks = max_blocks_per_seq;
   a.max_tokens = max_blocks_per_seq * block_size;
   a.sub_shift = block_size == 32 ? 1 : 0;
-  const hipError_t err = pkv::launch_decode(a, grid, head_dim, dtype == PKV_BF16, stream);
+  const hipError_t err =
+      pkv::launch_decode(a, grid, head_dim, dtype == PKV_BF16, kv_fp8, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  float scale, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int num_seqs, int max_blocks_per_seq,
+                                  int max_context_len, int num_workgroups, pkv_dtype dtype,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, scale, false, 1.0f, 1.0f,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_seqs,
+                     max_blocks_per_seq, max_context_len, num_workgroups, dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+pkv_status paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_tables,
+                                      const int32_t* context_lens, float scale, float k_scale,
+                                      float v_scale, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int num_seqs,
+                                      int max_blocks_per_seq, int max_context_len,
+                                      int num_workgroups, pkv_dtype dtype, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, scale, true, k_scale,
+                     v_scale, num_q_heads, num_kv_heads, head_dim, block_size, num_seqs,
+                     max_blocks_per_seq, max_context_len, num_workgroups, dtype, workspace,
+                     workspace_bytes, stream);
 }
 
 const char* pkv_status_string(pkv_status status) {

@@ -13,12 +13,14 @@ namespace pkv {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const unsigned short* __restrict__ key, const unsigned short* __restrict__ value,
     unsigned short* __restrict__ k_pool, unsigned short* __restrict__ v_pool,
-    const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads, int block_size) {
+    const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads, int block_size,
+    int64_t num_slots) {
   constexpr int kChunks = D / 8;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long total = (long)num_tokens * num_kv_heads * kChunks;
@@ -28,7 +30,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int h = (int)(r % num_kv_heads);
   const long i = r / num_kv_heads;
   const int64_t slot = slot_mapping[i];
-  if (slot < 0) return;
+  if (slot < 0 || slot >= num_slots) return;  // skipped: negative or past the pool
   const int64_t b = slot / block_size;
   const int tb = (int)(slot % block_size);
   const int t = tb % kBlock;  // token within its 16-token sub-tile
@@ -49,6 +51,98 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   for (int e = 0; e < 8; ++e) {
     const unsigned short bits = (unsigned short)(words[e / 2] >> (16 * (e % 2)));
     v_pool[base + (size_t)e * 8] = bits;  // d%16 + 1 -> +2*4 elements
+  }
+}
+
+// OCP E4M3 code of an fp32 value: round to nearest even, saturating at +-448, NaN kept (with its
+// sign), sign kept for zero. Integer arithmetic on the fp32 bits, so every device gives the same
+// code.
+__device__ __forceinline__ unsigned e4m3_code(float y) {
+  const unsigned bits = __float_as_uint(y);
+  const unsigned sign = (bits >> 24) & 0x80u;
+  const unsigned a = bits & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;  // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu; // |y| >= 448 (and infinity): saturate
+  const int e = (int)(a >> 23) - 127;        // exponent of |y| (fp32 denormals: -127)
+  if (e < -6) {
+    // Below the smallest normal 2^-6: code = |y| * 2^9 rounded, i.e. the 24-bit significand
+    // shifted right by 14 - e bits (a result of 8 is the smallest normal, code 0x08).
+    const int sh = 14 - e;
+    if (sh >= 32) return sign;
+    const unsigned sig = (a & 0x7FFFFFu) | 0x800000u;
+    unsigned q = sig >> sh;
+    const unsigned rem = sig & ((1u << sh) - 1u);
+    const unsigned half = 1u << (sh - 1);
+    q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+    return sign | q;
+  }
+  // Normal: 3 mantissa bits from 23, exponent field e + 7.
+  const unsigned m = a & 0x7FFFFFu;
+  unsigned q = m >> 20;
+  const unsigned rem = m & 0xFFFFFu;
+  q += (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
+  unsigned ef = (unsigned)(e + 7);
+  if (q == 8u) {
+    q = 0u;
+    ++ef;
+  }
+  return sign | (ef << 3) | q;
+}
+
+// reshape_and_cache into fp8 pools: one thread quantizes eight consecutive dims of one (token,
+// kv head): K is one 8-byte store (the fp8 K tile keeps those eight dims contiguous), V eight
+// byte stores (the fp8 V tile keeps four consecutive tokens of a dim together).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const unsigned short* __restrict__ key, const unsigned short* __restrict__ value,
+    unsigned char* __restrict__ k_pool, unsigned char* __restrict__ v_pool,
+    const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads, int block_size,
+    int64_t num_slots, float k_inv, float v_inv) {
+  constexpr int kChunks = D / 8;
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long total = (long)num_tokens * num_kv_heads * kChunks;
+  if (gid >= total) return;
+  const int c = (int)(gid % kChunks);
+  const long r = gid / kChunks;
+  const int h = (int)(r % num_kv_heads);
+  const long i = r / num_kv_heads;
+  const int64_t slot = slot_mapping[i];
+  if (slot < 0 || slot >= num_slots) return;  // skipped: negative or past the pool
+  const int64_t b = slot / block_size;
+  const int tb = (int)(slot % block_size);
+  const int t = tb % kBlock;
+  const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)block_size * D +
+                      (size_t)(tb / kBlock) * (kBlock * D);
+  const size_t src = ((size_t)i * num_kv_heads + h) * D + 8 * c;
+  const u32x4 kw = *(const u32x4*)(key + src);
+  const u32x4 vw = *(const u32x4*)(value + src);
+  const unsigned kwords[4] = {kw.x, kw.y, kw.z, kw.w};
+  const unsigned vwords[4] = {vw.x, vw.y, vw.z, vw.w};
+  auto widen = [](unsigned short bits) -> float {
+    if constexpr (BF16) {
+      return __uint_as_float((unsigned)bits << 16);
+    } else {
+      return (float)__builtin_bit_cast(_Float16, bits);
+    }
+  };
+  const int d0 = 8 * c;
+  unsigned kc[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const unsigned short kb = (unsigned short)(kwords[e / 2] >> (16 * (e % 2)));
+    kc[e / 4] |= e4m3_code(widen(kb) * k_inv) << (8 * (e % 4));
+  }
+  // K: [d/64][(d/8)%4][token][(d/32)%2][d%8] -> dims d0..d0+7 are 8 contiguous bytes
+  const size_t koff = tile + (size_t)(d0 / 64) * 1024 + (size_t)(16 * ((d0 / 8) % 4) + t) * 16 +
+                      (size_t)((d0 / 32) % 2) * 8;
+  *(u32x2*)(k_pool + koff) = u32x2{kc[0], kc[1]};
+  // V: [d/64][token/4][d%16][(d/16)%4][token%4]
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = d0 + e;
+    const unsigned short vb = (unsigned short)(vwords[e / 2] >> (16 * (e % 2)));
+    v_pool[tile + (size_t)(d / 64) * 1024 + (size_t)((t / 4) * 16 + d % 16) * 16 +
+           (size_t)((d / 16) % 4) * 4 + t % 4] = (unsigned char)e4m3_code(widen(vb) * v_inv);
   }
 }
 
@@ -85,9 +179,37 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, size_t layer_bytes, si
   return hipGetLastError();
 }
 
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_pool,
+                                        void* v_pool, const int64_t* slot_mapping, int num_tokens,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, bool src_bf16, float k_inv_scale,
+                                        float v_inv_scale, hipStream_t stream) {
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  const long total = (long)num_tokens * num_kv_heads * (head_dim / 8);
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const auto* k = (const unsigned short*)key;
+  const auto* v = (const unsigned short*)value;
+  auto* kp = (unsigned char*)k_pool;
+  auto* vp = (unsigned char*)v_pool;
+#define PKV_RC8(DD, BB)                                                                          \
+  hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<DD, BB>), dim3(blocks), dim3(256), 0, stream, \
+                     k, v, kp, vp, slot_mapping, num_tokens, num_kv_heads, block_size,           \
+                     num_slots, k_inv_scale, v_inv_scale)
+  if (head_dim == 128) {
+    if (src_bf16) PKV_RC8(128, true); else PKV_RC8(128, false);
+  } else {
+    if (src_bf16) PKV_RC8(64, true); else PKV_RC8(64, false);
+  }
+#undef PKV_RC8
+  return hipGetLastError();
+}
+
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
-                                    int head_dim, int block_size, hipStream_t stream) {
+                                    int head_dim, int block_size, int num_blocks,
+                                    hipStream_t stream) {
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
   const long total = (long)num_tokens * num_kv_heads * (head_dim / 8);
   if (total == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((total + 255) / 256);
@@ -97,10 +219,10 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   auto* vp = (unsigned short*)v_pool;
   if (head_dim == 128) {
     hipLaunchKernelGGL(reshape_and_cache_kernel<128>, dim3(blocks), dim3(256), 0, stream, k, v, kp,
-                       vp, slot_mapping, num_tokens, num_kv_heads, block_size);
+                       vp, slot_mapping, num_tokens, num_kv_heads, block_size, num_slots);
   } else {
     hipLaunchKernelGGL(reshape_and_cache_kernel<64>, dim3(blocks), dim3(256), 0, stream, k, v, kp,
-                       vp, slot_mapping, num_tokens, num_kv_heads, block_size);
+                       vp, slot_mapping, num_tokens, num_kv_heads, block_size, num_slots);
   }
   return hipGetLastError();
 }

@@ -49,8 +49,10 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // A score may exceed the reference maximum by this much (log2 units) before the reference moves.
@@ -93,6 +95,12 @@ struct Elem<true> {
   static __device__ __forceinline__ unsigned short store(float x) {
     return __builtin_bit_cast(unsigned short, (__bf16)x);
   }
+  // Four E4M3 codes (bytes 0..3 of w) -> four bf16 in two dwords (exact: E4M3 is a subset).
+  static __device__ __forceinline__ u32x2 from_fp8(unsigned w) {
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+  }
 };
 
 template <>
@@ -117,6 +125,12 @@ struct Elem<false> {
   }
   static __device__ __forceinline__ unsigned short store(float x) {
     return __builtin_bit_cast(unsigned short, (_Float16)x);
+  }
+  // Four E4M3 codes -> four fp16 (exact: every E4M3 value is an fp16 value).
+  static __device__ __forceinline__ u32x2 from_fp8(unsigned w) {
+    const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+    return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
   }
 };
 
@@ -146,14 +160,15 @@ __device__ __forceinline__ int range_owner(int p, int nwg, int W) {
   return (int)(((long)(p + 1) * nwg - 1) / W);
 }
 
-template <int D, bool BF16, int RING>
+template <int D, bool BF16, bool KV8, int RING>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void
 paged_decode_kernel(DecodeLaunch a) {
   using E = Elem<BF16>;
-  constexpr int NQ = D / 32;   // 16-byte K loads (and QK matrix ops) per block
-  constexpr int NV = D / 32;   // 16-byte V loads per block
-  constexpr int NO = D / 16;   // 16-column output chunks
-  constexpr size_t kTileBytes = (size_t)kBlock * D * 2;
+  constexpr int NQ = D / 32;                 // QK matrix ops (32-dim chunks) per block
+  constexpr int NK = KV8 ? D / 64 : D / 32;  // 16-byte K loads per block
+  constexpr int NV = KV8 ? D / 64 : D / 32;  // 16-byte V loads per block
+  constexpr int NO = D / 16;                 // 16-column output chunks
+  constexpr size_t kTileBytes = (size_t)kBlock * D * (KV8 ? 1 : 2);  // one 16-token sub-tile
   constexpr int kRow = D + 4;  // LDS row stride (floats) of the combine buffer
   constexpr int kThreads = 64 * kWaves;
   constexpr int kHeadsPerWave = kMaxGroupTile / kWaves;   // 4 heads per wave in the combine
@@ -373,7 +388,7 @@ paged_decode_kernel(DecodeLaunch a) {
 
   // Normalise and store kDims consecutive dims of output row `row`.
   auto store_out = [&](size_t row, const float* acc, float L) {
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float inv = L > 0.f ? a.v_scale / L : 0.f;  // v_scale: fp8 V pool scale (else 1)
     unsigned short r[kDims];
 #pragma unroll
     for (int i = 0; i < kDims; ++i) r[i] = E::store(acc[i] * inv);
@@ -529,13 +544,13 @@ paged_decode_kernel(DecodeLaunch a) {
   };
 
   // Ring of RING tile buffers: block m + RING - 1 is loading while block m is computed.
-  u32x4 kr[RING][NQ], vr[RING][NV];
+  u32x4 kr[RING][NK], vr[RING][NV];
   auto issue = [&](int m, u32x4* kd, u32x4* vd) {
     const unsigned t = tile_of(m);
     const char* kp = kbase + (size_t)t * kTileBytes;
     const char* vp = vbase + (size_t)t * kTileBytes;
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) kd[c] = load16_stream(kp + c * 1024);
+    for (int c = 0; c < NK; ++c) kd[c] = load16_stream(kp + c * 1024);
 #pragma unroll
     for (int c = 0; c < NV; ++c) vd[c] = load16_stream(vp + c * 1024);
   };
@@ -556,7 +571,17 @@ paged_decode_kernel(DecodeLaunch a) {
     // Scores: lane holds S[token 4kg + e][head hl], e = 0..3.
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) sc = E::qk(kc[c], qv[c], sc);
+    for (int c = 0; c < NQ; ++c) {
+      if constexpr (KV8) {
+        // fp8 K: load c/2 holds this lane's 8 dims of chunks c (bytes 0..7) and c+1 (8..15).
+        const u32x4 w = kc[c / 2];
+        const u32x2 lo = E::from_fp8((c & 1) ? w.z : w.x);
+        const u32x2 hi = E::from_fp8((c & 1) ? w.w : w.y);
+        sc = E::qk(u32x4{lo.x, lo.y, hi.x, hi.y}, qv[c], sc);
+      } else {
+        sc = E::qk(kc[c], qv[c], sc);
+      }
+    }
 
     const int tb = j * kBlock + 4 * kg;  // token of element e = 0
     float x[4];
@@ -588,22 +613,42 @@ paged_decode_kernel(DecodeLaunch a) {
 
     // Ragged last block: zero V of dead slots (they may hold anything, NaN included).
     if ((j + 1) * kBlock > cur.n) {
-      const unsigned m01 = (tb + 0 < cur.n ? 0x0000FFFFu : 0u) | (tb + 1 < cur.n ? 0xFFFF0000u : 0u);
-      const unsigned m23 = (tb + 2 < cur.n ? 0x0000FFFFu : 0u) | (tb + 3 < cur.n ? 0xFFFF0000u : 0u);
+      if constexpr (KV8) {
+        // each dword is 4 tokens (one byte each) of one dim
+        const unsigned m8 = (tb + 0 < cur.n ? 0x000000FFu : 0u) | (tb + 1 < cur.n ? 0x0000FF00u : 0u) |
+                            (tb + 2 < cur.n ? 0x00FF0000u : 0u) | (tb + 3 < cur.n ? 0xFF000000u : 0u);
 #pragma unroll
-      for (int c = 0; c < NV; ++c) {
-        vc[c].x &= m01;
-        vc[c].y &= m23;
-        vc[c].z &= m01;
-        vc[c].w &= m23;
+        for (int c = 0; c < NV; ++c) {
+          vc[c].x &= m8;
+          vc[c].y &= m8;
+          vc[c].z &= m8;
+          vc[c].w &= m8;
+        }
+      } else {
+        const unsigned m01 = (tb + 0 < cur.n ? 0x0000FFFFu : 0u) | (tb + 1 < cur.n ? 0xFFFF0000u : 0u);
+        const unsigned m23 = (tb + 2 < cur.n ? 0x0000FFFFu : 0u) | (tb + 3 < cur.n ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          vc[c].x &= m01;
+          vc[c].y &= m23;
+          vc[c].z &= m01;
+          vc[c].w &= m23;
+        }
       }
     }
 
     // O[head][16i + col] += P[head][token] V[token][16i + col]
 #pragma unroll
     for (int i = 0; i < NO; ++i) {
-      const u32x4 w = vc[i / 2];
-      const u32x2 vv = (i & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
+      u32x2 vv;
+      if constexpr (KV8) {
+        // fp8 V: load i/4, dword i%4 holds this lane's 4 tokens of dim 16i + hl.
+        const u32x4 w = vc[i / 4];
+        vv = E::from_fp8((i & 3) == 0 ? w.x : (i & 3) == 1 ? w.y : (i & 3) == 2 ? w.z : w.w);
+      } else {
+        const u32x4 w = vc[i / 2];
+        vv = (i & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
+      }
       o[i] = E::pv(phi, vv, o[i]);
       o[i] = E::pv(plo, vv, o[i]);
     }
@@ -658,22 +703,30 @@ paged_decode_kernel(DecodeLaunch a) {
   }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool KV8>
 hipError_t launch_typed(const DecodeLaunch& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_kernel<D, BF16, kRing<D>>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((paged_decode_kernel<D, BF16, KV8, kRing<D>>), dim3((unsigned)grid),
                      dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
+template <int D, bool KV8>
+hipError_t launch_dtype(const DecodeLaunch& a, int grid, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_typed<D, true, KV8>(a, grid, stream)
+              : launch_typed<D, false, KV8>(a, grid, stream);
+}
+
 }  // namespace
 
-hipError_t launch_decode(const DecodeLaunch& a, int grid, int head_dim, bool bf16,
+hipError_t launch_decode(const DecodeLaunch& a, int grid, int head_dim, bool bf16, bool kv_fp8,
                          hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
   if (head_dim == 128) {
-    return bf16 ? launch_typed<128, true>(a, grid, stream) : launch_typed<128, false>(a, grid, stream);
+    return kv_fp8 ? launch_dtype<128, true>(a, grid, bf16, stream)
+                  : launch_dtype<128, false>(a, grid, bf16, stream);
   }
-  return bf16 ? launch_typed<64, true>(a, grid, stream) : launch_typed<64, false>(a, grid, stream);
+  return kv_fp8 ? launch_dtype<64, true>(a, grid, bf16, stream)
+                : launch_dtype<64, false>(a, grid, bf16, stream);
 }
 
 }  // namespace pkv

@@ -24,7 +24,8 @@ struct DecodeLaunch {
   unsigned* counters;   // [grid] arrival counts of split streams; zero between launches
   float* ws_o;          // [grid][2][16][D] unnormalised partial outputs of split streams
   float* ws_ml;         // [grid][2][16][2] (reference max in log2 units, row sum)
-  float scale_log2;     // scale * log2(e)
+  float scale_log2;     // scale * log2(e) (times the K pool scale for fp8 pools)
+  float v_scale;        // V pool scale for fp8 pools, else 1
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
@@ -36,8 +37,15 @@ struct DecodeLaunch {
 };
 
 // Launch the decode kernel on `grid` workgroups. Returns a hipError_t.
-hipError_t launch_decode(const DecodeLaunch& a, int grid, int head_dim, bool bf16,
+hipError_t launch_decode(const DecodeLaunch& a, int grid, int head_dim, bool bf16, bool kv_fp8,
                          hipStream_t stream);
+
+// reshape_and_cache into fp8 (E4M3) pools: code = e4m3(fl32(x * inv_scale)) per element.
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_pool,
+                                        void* v_pool, const int64_t* slot_mapping, int num_tokens,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, bool src_bf16, float k_inv_scale,
+                                        float v_inv_scale, hipStream_t stream);
 
 // Copy the K and V regions of blocks src[i] -> dst[i] in every layer (device arrays).
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, size_t layer_bytes, size_t block_bytes,
@@ -46,6 +54,7 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, size_t layer_bytes, si
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
-                                    int head_dim, int block_size, hipStream_t stream);
+                                    int head_dim, int block_size, int num_blocks,
+                                    hipStream_t stream);
 
 }  // namespace pkv

@@ -99,3 +99,59 @@ def poison_dead_slots_(k_layer: torch.Tensor, v_layer: torch.Tensor, tables, len
     ia = torch.tensor(idx, dtype=torch.long, device=k_layer.device)
     k_layer.view(-1)[ia[:, 0]] = float("nan")
     v_layer.view(-1)[ia[:, 1]] = float("nan")
+
+
+# ---- fp8 (E4M3) pools ----------------------------------------------------------------------
+
+def gpu_decode8(q, k_layer, v_layer, block_tables, context_lens, scale, k_scale, v_scale, Hq, Hkv,
+                max_ctx, num_workgroups=0, out=None, workspace=None, block_size=16):
+    D = q.shape[-1]
+    S = q.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, block_size, max_ctx,
+                                                     num_workgroups)
+        workspace = pkv.new_workspace(nbytes, q.device)
+    pkv.paged_attention_decode_fp8(out, q, k_layer, v_layer, block_tables, context_lens, scale,
+                                   k_scale, v_scale, Hq, Hkv, D, block_size, max_ctx,
+                                   num_workgroups, workspace)
+    return out
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    """Raw bytes of a (device or host) uint8 pool as a host numpy array."""
+    return t.detach().contiguous().cpu().numpy().view(np.uint8)
+
+
+def oracle_decode8(q, k_layer, v_layer, block_tables, context_lens, scale, k_scale, v_scale, Hq,
+                   Hkv, num_blocks, pairs=None, block_size=16):
+    kb = codes(k_layer) if isinstance(k_layer, torch.Tensor) else k_layer
+    vb = codes(v_layer) if isinstance(v_layer, torch.Tensor) else v_layer
+    bt = block_tables.cpu().numpy() if isinstance(block_tables, torch.Tensor) else block_tables
+    cl = context_lens.cpu().numpy() if isinstance(context_lens, torch.Tensor) else context_lens
+    return oracle.paged_decode8(words(q), kb, vb, k_scale, v_scale, bt, cl, scale, Hq, Hkv,
+                                q.shape[-1], block_size, num_blocks, oracle_dtype(q), pairs=pairs,
+                                threads=host_threads())
+
+
+def poison_dead_slots8_(k_layer: torch.Tensor, v_layer: torch.Tensor, tables, lens,
+                        num_kv_heads: int, head_dim: int, block_size: int = 16):
+    """Write the E4M3 NaN code into the unwritten slots of every sequence's last block."""
+    B = block_size
+    idx = []
+    for s, n in enumerate(lens):
+        n = int(n)
+        if n % B == 0:
+            continue
+        b = int(tables[s][n // B])
+        for t in range(n % B, B):
+            for h in range(num_kv_heads):
+                for d in range(head_dim):
+                    idx.append((oracle.pool_index8(False, b, h, t, d, num_kv_heads, B, head_dim),
+                                oracle.pool_index8(True, b, h, t, d, num_kv_heads, B, head_dim)))
+    if not idx:
+        return
+    ia = torch.tensor(idx, dtype=torch.long, device=k_layer.device)
+    k_layer.view(-1)[ia[:, 0]] = 0x7F
+    v_layer.view(-1)[ia[:, 1]] = 0x7F

@@ -247,3 +247,20 @@ def test_block_size_32_reshape_and_cache_bit_exact(D):
     pkv.reshape_and_cache(b.new_key, b.new_value, k, v, b.slot_mapping, t.num_blocks, 32)
     torch.cuda.synchronize()
     assert np.array_equal(words(k), kw) and np.array_equal(words(v), vw)
+
+
+def test_reshape_and_cache_skips_negative_and_past_pool_slots():
+    spec, t, b = _random_case(4, 2, 128, [5, 9, 20, 33], seed=31)
+    k, v = _layer(b)
+    sm = b.slot_mapping.clone()
+    sm[0] = -1
+    sm[2] = t.num_blocks * 16      # first slot past the sub-pool: skipped
+    kw, vw = words(k), words(v)
+    sm_oracle = sm.cpu().clone()
+    sm_oracle[2] = -1
+    oracle.reshape_and_cache(kw, vw, b.new_key.cpu(), b.new_value.cpu(), sm_oracle, 2, 128, 16,
+                             t.num_blocks)
+    say("reshape negative and past-pool slots")
+    pkv.reshape_and_cache(b.new_key, b.new_value, k, v, sm, t.num_blocks)
+    torch.cuda.synchronize()
+    assert np.array_equal(words(k), kw) and np.array_equal(words(v), vw)

@@ -1,6 +1,7 @@
 """Host-side invariants of the seeded decode inputs (no GPU needed)."""
 import numpy as np
 import pytest
+import torch
 
 import workloads
 from workloads import SPECS, append_step, make_tables
@@ -102,3 +103,15 @@ def test_make_batch_cpu_small():
     assert b.k_pool[0, unused].isnan().all() and not b.k_pool[0, ~unused].isnan().any()
     b2 = workloads.make_batch(spec)
     assert b.q.equal(b2.q) and b.new_key.equal(b2.new_key)
+
+
+def test_random_e4m3_codes_are_finite_and_bounded():
+    import oracle
+    g = torch.Generator().manual_seed(3)
+    c = workloads.random_e4m3_codes(1 << 16, g, "cpu").numpy()
+    assert c.dtype == np.uint8
+    assert not np.any((c & 0x7F) == 0x7F), "NaN code drawn"
+    vals = np.array([oracle.e4m3_value(int(x)) for x in range(256)])
+    v = vals[c]
+    assert np.all(np.isfinite(v)) and np.max(np.abs(v)) <= 3.75
+    assert len(np.unique(c)) == 2 * 9 * 8      # every sign / exponent 0..8 / mantissa drawn

@@ -222,6 +222,56 @@ def fill_pool_(pool: torch.Tensor, generator: torch.Generator, chunk_elems: int 
     return pool
 
 
+E4M3_NAN = 0x7F   # the NaN code of OCP E4M3, written into unused fp8 pool blocks
+
+
+def random_e4m3_codes(n: int, generator: torch.Generator, device) -> torch.Tensor:
+    """n random 8-bit E4M3 codes (uint8): random sign, exponent field uniform in 0..8, mantissa
+    uniform in 0..7, so the magnitudes lie in [0, 3.75] and no code is NaN."""
+    kw = dict(generator=generator, device=device, dtype=torch.uint8)
+    sign = torch.randint(0, 2, (n,), **kw)
+    expo = torch.randint(0, 9, (n,), **kw)
+    mant = torch.randint(0, 8, (n,), **kw)
+    return (sign << 7) | (expo << 3) | mant
+
+
+def fill_pool_fp8_(pool: torch.Tensor, generator: torch.Generator, chunk: int = 1 << 30):
+    """Fill a uint8 pool with random_e4m3_codes in chunks."""
+    flat = pool.view(-1)
+    for start in range(0, flat.numel(), chunk):
+        stop = min(start + chunk, flat.numel())
+        flat[start:stop] = random_e4m3_codes(stop - start, generator, pool.device)
+    return pool
+
+
+def make_batch_fp8(spec: Spec, device="cpu", tables: Optional[Tables] = None,
+                   seed: Optional[int] = None) -> Batch:
+    """As make_batch, with fp8 pools: uint8 [L][NB][Hkv][B*D] of random E4M3 codes and the NaN
+    code in blocks no table references. q, new_key and new_value stay 16-bit."""
+    if tables is None:
+        tables = make_tables(spec)
+    Hq, Hkv, D, B = spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size
+    S = tables.context_lens.shape[0]
+    L, NB = spec.num_layers, tables.num_blocks
+    g = torch.Generator(device=device)
+    g.manual_seed((spec.seed if seed is None else seed) * 7919 + 23)
+    dt = spec.torch_dtype
+    q = randn((S, Hq, D), dt, g, device)
+    k_pool = fill_pool_fp8_(torch.empty((L, NB, Hkv, B * D), dtype=torch.uint8, device=device), g)
+    v_pool = fill_pool_fp8_(torch.empty((L, NB, Hkv, B * D), dtype=torch.uint8, device=device), g)
+    if not tables.used_blocks.all():
+        unused = torch.from_numpy(np.nonzero(~tables.used_blocks)[0]).to(device)
+        k_pool[:, unused] = E4M3_NAN
+        v_pool[:, unused] = E4M3_NAN
+    T = tables.slot_mapping.shape[0]
+    new_key = randn((T, Hkv, D), dt, g, device)
+    new_value = randn((T, Hkv, D), dt, g, device)
+    return Batch(spec, tables, q, k_pool, v_pool, new_key, new_value,
+                 torch.from_numpy(tables.block_tables).to(device),
+                 torch.from_numpy(tables.context_lens).to(device),
+                 torch.from_numpy(tables.slot_mapping).to(device))
+
+
 def make_batch(spec: Spec, device="cpu", tables: Optional[Tables] = None,
                poison_unused: bool = True, seed: Optional[int] = None) -> Batch:
     """Full seeded input of one decode step: q, both pools (all layers), new K/V, tables."""
