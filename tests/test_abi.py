@@ -173,3 +173,51 @@ def test_copy_blocks_argument_errors():
     assert f(pool._h, None, FAKE, 1, None) == INVALID
     assert f(pool._h, FAKE + 2, FAKE, 1, None) == ALIGN
     pool.destroy()
+
+
+def test_fp8_pool_sizing_and_argument_errors():
+    lib = pkv.load_library()
+    FP8 = pkv.PKV_FP8_E4M3
+    each = pkv.kv_pool_bytes(80, 16384, 8, 128, 16, FP8)
+    assert 2 * each == sizing.kv_bytes(80, 8, 128, 64 * 4096, 1)
+    assert each == pkv.kv_pool_bytes(80, 16384, 8, 128, 16, pkv.PKV_BF16) // 2
+    pool = pkv.kv_pool_create(FAKE, FAKE * 2, each, 80, 16384, 8, 128, 16, FP8)
+    k1, _ = pool.layer(1)
+    assert k1 - FAKE == 16384 * 8 * 16 * 128
+    pool.destroy()
+
+    r = lib.reshape_and_cache_fp8
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, pkv.PKV_BF16, 0.5, 0.5, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, x in kw.items():
+            a[int(i[1:])] = x
+        return r(*a)
+
+    assert call(a5=0) == OK                                  # no tokens
+    assert call(a11=0.0) == INVALID                          # scales must be finite and > 0
+    assert call(a12=-1.0) == INVALID
+    assert call(a11=float("inf")) == INVALID
+    assert call(a12=float("nan")) == INVALID
+    assert call(a10=FP8) == UNSUPPORTED                      # key/value are 16-bit
+    assert call(a7=96) == UNSUPPORTED
+    assert call(a9=0) == INVALID                             # empty pool
+    assert call(a2=FAKE + 8) == ALIGN
+
+    d = lib.paged_attention_decode_fp8
+
+    def dec(**kw):
+        a = dict(scale=0.1, ks=1.0, vs=1.0, dt=0, nwg=1, ws=None, wsb=0, s=4, d=128)
+        a.update(kw)
+        return d(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["scale"], a["ks"], a["vs"], 32, 8,
+                 a["d"], 16, a["s"], 8, 128, a["nwg"], a["dt"], a["ws"], a["wsb"], None)
+
+    assert dec(ks=0.0) == INVALID
+    assert dec(vs=float("inf")) == INVALID
+    assert dec(ks=-2.0) == INVALID
+    assert dec(dt=FP8) == UNSUPPORTED                        # q and out are 16-bit
+    assert dec(d=96) == UNSUPPORTED
+    assert dec(s=0) == OK
+    assert dec(nwg=32) == WORKSPACE
+    assert dec(nwg=32, ws=FAKE, wsb=_ws(32) - 1) == WORKSPACE
