@@ -177,6 +177,95 @@ def bench_copy_blocks(args) -> int:
     return 0
 
 
+PCIE_PEAK_GBS = 64.0    # PCIe 5.0 x16, per direction: the MI355X host link
+
+
+def bench_swap(args) -> int:
+    """Preemption by swapping on the 70B-shaped pool: the blocks of 2 of the batch's 64 sequences
+    (512 blocks) go to a pinned host pool and come back, every layer, K and V. Bytes per call =
+    pairs x layers x 2 x block bytes, each crossing the host link once."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_452_amd as pkv
+    import workloads
+
+    spec = workloads.SPECS[4]
+    t = workloads.make_tables(spec)
+    L, NB, Hkv, D, B = spec.num_layers, t.num_blocks, spec.num_kv_heads, spec.head_dim, 16
+    k = torch.empty((L, NB, Hkv, B * D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    victims = np.concatenate([t.block_tables[0], t.block_tables[1]]).astype(np.int32)
+    n = victims.shape[0]
+    hk = torch.empty((L, n, Hkv, B * D), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    dpool = pkv.kv_pool_create(k, v, k.numel() * 2, L, NB, Hkv, D, B, pkv.PKV_BF16)
+    hpool = pkv.kv_pool_create(hk, hv, hk.numel() * 2, L, n, Hkv, D, B, pkv.PKV_BF16)
+    dev_ids = torch.from_numpy(victims).cuda()
+    host_ids = torch.arange(n, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    moved = n * L * 2 * Hkv * B * D * 2
+
+    def timed(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    swap_out = lambda: pkv.swap_blocks(dpool, hpool, dev_ids, host_ids, pkv.PKV_SWAP_OUT, stream)
+    swap_in = lambda: pkv.swap_blocks(dpool, hpool, host_ids, dev_ids, pkv.PKV_SWAP_IN, stream)
+    for _ in range(max(1, args.warmup)):
+        swap_out()
+        swap_in()
+    reps = max(1, args.steps)
+    ms_out = timed(swap_out, reps)
+    ms_in = timed(swap_in, reps)
+    # The link's own ceiling on this box: one contiguous pinned copy of the same size each way
+    # (the runtime's DMA path).
+    flat_d = torch.empty(moved // 2, dtype=torch.bfloat16, device="cuda")
+    flat_h = torch.empty(moved // 2, dtype=torch.bfloat16, pin_memory=True)
+    flat_h.copy_(flat_d, non_blocking=True)
+    flat_d.copy_(flat_h, non_blocking=True)
+    ms_d2h = timed(lambda: flat_h.copy_(flat_d, non_blocking=True), reps)
+    ms_h2d = timed(lambda: flat_d.copy_(flat_h, non_blocking=True), reps)
+    gbs = lambda ms: moved / (ms * 1e-3) / 1e9
+    out_gbs, in_gbs = gbs(ms_out), gbs(ms_in)
+    rt = 2 * moved / ((ms_out + ms_in) * 1e-3) / 1e9
+    # CPU oracle beside it: the same block gather as numpy on host copies of 2 layers.
+    rng = np.random.default_rng(3)
+    kh = rng.integers(0, 65535, size=(2, NB, Hkv * B * D), dtype=np.uint16)
+    dst = np.zeros((2, n, Hkv * B * D), np.uint16)
+    t0 = time.perf_counter()
+    creps = 0
+    while time.perf_counter() - t0 < 2.0:
+        dst[:] = kh[:, victims]
+        creps += 1
+    cpu_gbs = 2 * n * Hkv * B * D * 2 / ((time.perf_counter() - t0) / creps) / 1e9
+    print(json.dumps({
+        "metric": "swap_blocks GB/s over the host link (swap out + swap in)", "value": round(rt, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "higher_is_better": True, "data": "synthetic", "dtype": "bf16",
+        "config": {"workload": "preempt 2 of 64 sequences of the 70B-shaped batch: 512 blocks x 80 "
+                               "layers x (K, V), 32 KiB per block region, to a pinned host pool "
+                               "and back", "bytes_per_call": moved},
+        "swap_out_ms": round(ms_out, 3), "swap_out_gbs": round(out_gbs, 2),
+        "swap_in_ms": round(ms_in, 3), "swap_in_gbs": round(in_gbs, 2),
+        "dma_copy_same_bytes": {"d2h_gbs": round(gbs(ms_d2h), 2), "h2d_gbs": round(gbs(ms_h2d), 2),
+                                "what": "one contiguous pinned hipMemcpyAsync each way"},
+        "roofline": {"bound": "host link", "achieved": round(rt, 2), "peak": PCIE_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(rt / PCIE_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                         "sample": "numpy gather of the same 512 blocks from host copies of 2 "
+                                   "layers of one pool"},
+    }), flush=True)
+    for p in (dpool, hpool):
+        p.destroy()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,8 +283,9 @@ def main() -> int:
                     help="pool element type: the model's 16-bit type (default) or E4M3 codes "
                          "with one scale per pool")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel", choices=["decode", "copy_blocks"], default="decode",
-                    help="decode (the hot path, default) or copy_blocks (copy-on-write copies)")
+    ap.add_argument("--kernel", choices=["decode", "copy_blocks", "swap"], default="decode",
+                    help="decode (the hot path, default), copy_blocks (copy-on-write copies) or "
+                         "swap (preemption to and from pinned host memory)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -212,6 +302,8 @@ def main() -> int:
         return calibrate_copy()
     if args.kernel == "copy_blocks":
         return bench_copy_blocks(args)
+    if args.kernel == "swap":
+        return bench_swap(args)
     pkv.load_library()
     dev = "cuda"
     spec = workloads.SPECS[args.config]

@@ -237,13 +237,45 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
  * and KV Cache Management" (blog.sejan.dev), section "Advanced Memory Sharing: Prefix Caching &
  * Copy-on-Write", part 2: a fresh block receives a copy of the shared block before the writer's
  * table points at it). Run it before the reshape_and_cache that writes into the copies.
- *   src_blocks, dst_blocks  device int32 [num_copies], 4-byte aligned, ids in [0, num_blocks).
- *                           A destination must not appear twice or also be a source (the order
- *                           of the copies is not defined). Not validated on the device.
+ *   src_blocks, dst_blocks  int32 [num_copies], 4-byte aligned, in device memory or pinned host
+ *                           memory (pageable memory is refused with PKV_ERR_INVALID_ARG). A pair
+ *                           with an id outside [0, num_blocks) is skipped on the device. A destination must not
+ *                           appear twice or also be a source (the order of the copies is not
+ *                           defined).
  * num_copies in [0, 65535]; 0 is a no-op.
  */
 pkv_status copy_blocks(const pkv_pool* pool, const int32_t* src_blocks, const int32_t* dst_blocks,
                        int num_copies, hipStream_t stream);
+
+/* Direction of swap_blocks. */
+typedef enum { PKV_SWAP_OUT = 0, PKV_SWAP_IN = 1 } pkv_swap_dir;
+
+/*
+ * Swapping for preemption ("KV-Cache Management and PagedAttention", section "What paging unlocks
+ * downstream", preemption and eviction; "PagedAttention and KV Cache Management", section
+ * "Continuous Batching vs. Static Batching", preemption and GPU swapping): whole blocks move
+ * between the device pool and a pool in host memory, K and V of every layer, bit-exact.
+ *   PKV_SWAP_OUT: for each i, block src_blocks[i] of device_pool -> block dst_blocks[i] of
+ *                 host_pool.
+ *   PKV_SWAP_IN:  block src_blocks[i] of host_pool -> block dst_blocks[i] of device_pool.
+ *   device_pool  a pool over device memory.
+ *   host_pool    a pool created by kv_pool_create over PINNED host memory (hipHostMalloc, or a
+ *                pinned torch tensor) with the same num_layers, num_kv_heads, head_dim,
+ *                block_size and dtype as device_pool; its num_blocks may differ. Same layout.
+ *   src_blocks, dst_blocks  int32 [num_pairs], 4-byte aligned, in device memory or pinned host
+ *                memory (pageable memory is refused). A pair with an id outside its pool is
+ *                skipped. Destinations must be
+ *                distinct and must not be sources.
+ * One kernel reads or writes the host pool across the host link, ordered on `stream`: synchronize
+ * the stream before reading swapped-out blocks on the host, and do not write the host blocks of a
+ * swap-in while it is in flight. num_pairs in [0, 65535]; 0 is a no-op.
+ * Errors: PKV_ERR_INVALID_ARG for null pools, mismatched geometry, a bad direction, or a host pool
+ * or id array that is not device-visible (pinned host or device) memory, detected before any
+ * launch.
+ */
+pkv_status swap_blocks(const pkv_pool* device_pool, const pkv_pool* host_pool,
+                       const int32_t* src_blocks, const int32_t* dst_blocks, int num_pairs,
+                       pkv_swap_dir direction, hipStream_t stream);
 
 /*
  * Host block manager: the bookkeeping of which physical blocks hold which sequence's tokens
@@ -260,11 +292,14 @@ pkv_status copy_blocks(const pkv_pool* pool, const int32_t* src_blocks, const in
  */
 typedef struct pkv_block_manager pkv_block_manager;
 
-/* A manager of num_blocks blocks of block_size tokens, all free (free list 0, 1, 2, ...). */
-pkv_status kv_block_manager_create(pkv_block_manager** out, int num_blocks, int block_size);
+/* A manager of num_blocks device blocks and num_host_blocks host blocks (for swapping; may be 0)
+ * of block_size tokens, all free (free lists 0, 1, 2, ...). */
+pkv_status kv_block_manager_create(pkv_block_manager** out, int num_blocks, int num_host_blocks,
+                                   int block_size);
 void kv_block_manager_destroy(pkv_block_manager* bm);  /* NULL is a no-op */
-/* Free blocks, or -1 for NULL. */
+/* Free device blocks / free host blocks, or -1 for NULL. */
 int kv_block_manager_num_free(const pkv_block_manager* bm);
+int kv_block_manager_num_free_host(const pkv_block_manager* bm);
 
 /* New sequence seq_id holding a prompt of num_tokens tokens: ceil(num_tokens / block_size)
  * blocks taken from the front of the free list. PKV_ERR_INVALID_ARG if seq_id exists,
@@ -289,14 +324,41 @@ pkv_status kv_block_manager_append(pkv_block_manager* bm, const int64_t* seq_ids
                                    int* num_copies);
 
 /* The sequence ends: each of its blocks loses one reference; blocks at zero go to the back of
- * the free list, in table order. */
+ * the free list, in table order (the host free list for a swapped-out sequence). */
 pkv_status kv_block_manager_release(pkv_block_manager* bm, int64_t seq_id);
+
+/*
+ * Preemption by swapping ("KV-Cache Management and PagedAttention", section "What paging unlocks
+ * downstream"; "PagedAttention and KV Cache Management", section "Continuous Batching vs. Static
+ * Batching"): the group seq_ids[0..num_seqs) (distinct, all on the device) moves to host blocks.
+ * Every distinct block of the group's tables, in order of first appearance (sequences in the
+ * given order, tables in logical order), takes one host block from the front of the host free
+ * list; pair k is (device_blocks[k] -> host_blocks[k]), *num_pairs pairs in host arrays of
+ * capacity max_pairs. Then each table entry drops its reference on its device block (blocks at
+ * zero go to the back of the free list, in that order) and points at the host block, so blocks
+ * shared inside the group stay shared. Run swap_blocks(PKV_SWAP_OUT) of the pairs before any
+ * freed device block is written again. A swapped-out sequence cannot be appended to, forked or
+ * passed to kv_block_manager_tables; it can be released or swapped in.
+ * PKV_ERR_NO_BLOCKS if the host free list is too short; PKV_ERR_INVALID_ARG for an unknown,
+ * repeated or already swapped-out id or too small a capacity. Nothing changes on an error.
+ */
+pkv_status kv_block_manager_swap_out(pkv_block_manager* bm, const int64_t* seq_ids, int num_seqs,
+                                     int32_t* device_blocks, int32_t* host_blocks, int max_pairs,
+                                     int* num_pairs);
+
+/* The reverse of kv_block_manager_swap_out for a group of swapped-out sequences: pairs
+ * (host_blocks[k] -> device_blocks[k]) with device blocks from the front of the free list; run
+ * swap_blocks(PKV_SWAP_IN) of the pairs before decoding the group. PKV_ERR_NO_BLOCKS if the
+ * device free list is too short. */
+pkv_status kv_block_manager_swap_in(pkv_block_manager* bm, const int64_t* seq_ids, int num_seqs,
+                                    int32_t* host_blocks, int32_t* device_blocks, int max_pairs,
+                                    int* num_pairs);
 
 /*
  * Decode inputs for seq_ids[0..num_seqs): row i of block_tables (host int32
  * [num_seqs][max_blocks_per_seq]) receives sequence i's physical blocks, padded with -1, and
- * context_lens[i] its token count. PKV_ERR_INVALID_ARG (nothing written) for an unknown id or a
- * table longer than max_blocks_per_seq.
+ * context_lens[i] its token count. PKV_ERR_INVALID_ARG (nothing written) for an unknown or
+ * swapped-out id or a table longer than max_blocks_per_seq.
  */
 pkv_status kv_block_manager_tables(const pkv_block_manager* bm, const int64_t* seq_ids,
                                    int num_seqs, int max_blocks_per_seq, int32_t* block_tables,

@@ -18,14 +18,17 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 PKV_BF16 = 0
 PKV_FP16 = 1
 PKV_FP8_E4M3 = 2
+PKV_SWAP_OUT = 0
+PKV_SWAP_IN = 1
 
 EXPORTED = ("kv_pool_bytes", "kv_pool_create", "kv_pool_layer", "kv_pool_destroy",
             "reshape_and_cache", "paged_attention_num_workgroups",
             "paged_attention_workspace_bytes", "paged_attention_decode", "copy_blocks",
-            "reshape_and_cache_fp8", "paged_attention_decode_fp8",
+            "reshape_and_cache_fp8", "paged_attention_decode_fp8", "swap_blocks",
             "kv_block_manager_create", "kv_block_manager_destroy", "kv_block_manager_num_free",
             "kv_block_manager_allocate", "kv_block_manager_fork", "kv_block_manager_append",
-            "kv_block_manager_release", "kv_block_manager_tables", "pkv_status_string")
+            "kv_block_manager_release", "kv_block_manager_tables", "kv_block_manager_num_free_host",
+            "kv_block_manager_swap_out", "kv_block_manager_swap_in", "pkv_status_string")
 
 PKV_ERR_NO_BLOCKS = -6
 
@@ -74,14 +77,21 @@ def load_library(build_if_missing: bool = True):
                                                i, i, i, vp, sz, vp]
     lib.paged_attention_decode_fp8.restype = i
     lib.copy_blocks.argtypes = [vp, vp, vp, i, vp]
+    lib.swap_blocks.argtypes = [vp, vp, vp, vp, i, i, vp]
+    lib.swap_blocks.restype = i
     lib.copy_blocks.restype = i
     i64 = ctypes.c_int64
-    lib.kv_block_manager_create.argtypes = [ctypes.POINTER(vp), i, i]
+    lib.kv_block_manager_create.argtypes = [ctypes.POINTER(vp), i, i, i]
     lib.kv_block_manager_create.restype = i
     lib.kv_block_manager_destroy.argtypes = [vp]
     lib.kv_block_manager_destroy.restype = None
     lib.kv_block_manager_num_free.argtypes = [vp]
     lib.kv_block_manager_num_free.restype = i
+    lib.kv_block_manager_num_free_host.argtypes = [vp]
+    lib.kv_block_manager_num_free_host.restype = i
+    for fn in (lib.kv_block_manager_swap_out, lib.kv_block_manager_swap_in):
+        fn.argtypes = [vp, vp, i, vp, vp, i, ctypes.POINTER(i)]
+        fn.restype = i
     lib.kv_block_manager_allocate.argtypes = [vp, i64, i64]
     lib.kv_block_manager_allocate.restype = i
     lib.kv_block_manager_fork.argtypes = [vp, i64, i64]
@@ -275,6 +285,26 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, block_tables, context_len
         _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def swap_blocks(device_pool: "KVPool", host_pool: "KVPool", src_blocks, dst_blocks,
+                direction: int, stream=None) -> None:
+    """Copy whole blocks between a device pool and a pinned host pool of the same geometry
+    (PKV_SWAP_OUT: device -> host, PKV_SWAP_IN: host -> device). src_blocks, dst_blocks: int32
+    tensors on the device or in pinned host memory."""
+    import torch
+    for t in (src_blocks, dst_blocks):
+        if isinstance(t, torch.Tensor):
+            if t.dtype != torch.int32 or not t.is_contiguous():
+                raise ValueError("block ids must be contiguous int32")
+            if not t.is_cuda and not t.is_pinned():
+                raise ValueError("block ids must be on the device or in pinned host memory")
+    n = int(src_blocks.numel())
+    if int(dst_blocks.numel()) != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    _check("swap_blocks", load_library().swap_blocks(device_pool._h, host_pool._h,
+                                                     _ptr(src_blocks), _ptr(dst_blocks), n,
+                                                     int(direction), _stream(stream)))
+
+
 def copy_blocks(pool: "KVPool", src_blocks, dst_blocks, stream=None) -> None:
     """Copy blocks src_blocks[i] -> dst_blocks[i] (device int32 tensors) in every layer of the
     pool's K and V (the device half of copy-on-write)."""
@@ -288,14 +318,15 @@ def copy_blocks(pool: "KVPool", src_blocks, dst_blocks, stream=None) -> None:
 
 
 class BlockManager:
-    """Host block manager (kv_block_manager_*): blocks of one pool, per-sequence tables, fork and
-    copy-on-write. Plain numpy in and out; no device work."""
+    """Host block manager (kv_block_manager_*): blocks of one pool, per-sequence tables, fork,
+    copy-on-write, and swapping to num_host_blocks host blocks. Plain numpy in and out; no device
+    work."""
 
-    def __init__(self, num_blocks: int, block_size: int = 16):
+    def __init__(self, num_blocks: int, block_size: int = 16, num_host_blocks: int = 0):
         lib = load_library()
         h = ctypes.c_void_p()
-        _check("kv_block_manager_create", lib.kv_block_manager_create(ctypes.byref(h), num_blocks,
-                                                                      block_size))
+        _check("kv_block_manager_create", lib.kv_block_manager_create(
+            ctypes.byref(h), num_blocks, num_host_blocks, block_size))
         self._h = h
         self.num_blocks = num_blocks
         self.block_size = block_size
@@ -311,6 +342,32 @@ class BlockManager:
     @property
     def num_free(self) -> int:
         return int(load_library().kv_block_manager_num_free(self._h))
+
+    @property
+    def num_free_host(self) -> int:
+        return int(load_library().kv_block_manager_num_free_host(self._h))
+
+    def _move(self, name: str, seq_ids, capacity: int):
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+        src = np.zeros(max(capacity, 1), np.int32)
+        dst = np.zeros(max(capacity, 1), np.int32)
+        k = ctypes.c_int(0)
+        vp = ctypes.c_void_p
+        _check(name, getattr(load_library(), name)(
+            self._h, ids.ctypes.data_as(vp), ids.shape[0], src.ctypes.data_as(vp),
+            dst.ctypes.data_as(vp), capacity, ctypes.byref(k)))
+        return np.stack([src[:k.value], dst[:k.value]], axis=1)
+
+    def swap_out(self, seq_ids):
+        """Move the group to host blocks. Returns int32 [k][2] (device block, host block) pairs
+        for swap_blocks(PKV_SWAP_OUT)."""
+        return self._move("kv_block_manager_swap_out", seq_ids, self.num_blocks)
+
+    def swap_in(self, seq_ids):
+        """Bring the group back. Returns int32 [k][2] (host block, device block) pairs for
+        swap_blocks(PKV_SWAP_IN)."""
+        return self._move("kv_block_manager_swap_in", seq_ids, self.num_blocks)
 
     def allocate(self, seq_id: int, num_tokens: int) -> None:
         _check("kv_block_manager_allocate",

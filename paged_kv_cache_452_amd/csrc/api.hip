@@ -40,6 +40,55 @@ size_t elem_bytes(pkv_dtype dtype) { return dtype == PKV_FP8_E4M3 ? 1 : 2; }
 
 bool valid_scale(float s) { return isfinite(s) && s > 0.f; }
 
+// Device address of a pinned (page-locked, device-mapped) host range [p, p + bytes): both ends
+// must be host memory known to the runtime. False for pageable or device memory; a failed query
+// is cleared so that it does not surface as the error of a later launch.
+bool pinned_device_address(const char* p, size_t bytes, void** dev) {
+  const char* ends[2] = {p, p + bytes - 1};
+  for (const char* e : ends) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, e) != hipSuccess || at.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return false;
+    }
+  }
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, (void*)p, 0) != hipSuccess || d == nullptr) {
+    (void)hipGetLastError();
+    return false;
+  }
+  *dev = d;
+  return true;
+}
+
+// Device-visible address of an id array: device memory as is, pinned host memory through its
+// device address. False for pageable host memory (a kernel would fault on it) or an unknown
+// pointer.
+bool device_visible(const int32_t* p, const int32_t** dev) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *dev = p;
+    return true;
+  }
+  if (at.type != hipMemoryTypeHost) return false;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, (void*)p, 0) != hipSuccess || d == nullptr) {
+    (void)hipGetLastError();
+    return false;
+  }
+  *dev = (const int32_t*)d;
+  return true;
+}
+
+// Bytes of one block's region in one layer of one of the two pools.
+size_t block_bytes_of(const pkv_pool* p) {
+  return (size_t)p->num_kv_heads * p->block_size * p->head_dim * elem_bytes(p->dtype);
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // a * b with overflow detection (all operands non-negative).
@@ -209,11 +258,64 @@ pkv_status copy_blocks(const pkv_pool* pool, const int32_t* src_blocks, const in
   if (src_blocks == nullptr || dst_blocks == nullptr) return PKV_ERR_INVALID_ARG;
   if (((uintptr_t)src_blocks & 3u) || ((uintptr_t)dst_blocks & 3u)) return PKV_ERR_ALIGNMENT;
   if (pool->num_layers > 32767) return PKV_ERR_UNSUPPORTED;
-  const size_t block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim *
-                             elem_bytes(pool->dtype);
-  const hipError_t err = pkv::launch_copy_blocks(pool->k, pool->v, pool->layer_bytes, block_bytes,
-                                                 pool->num_layers, src_blocks, dst_blocks,
-                                                 num_copies, stream);
+  const int32_t* src_dev = nullptr;
+  const int32_t* dst_dev = nullptr;
+  if (!device_visible(src_blocks, &src_dev) || !device_visible(dst_blocks, &dst_dev))
+    return PKV_ERR_INVALID_ARG;
+  pkv::BlockCopy c;
+  c.src_k = pool->k;
+  c.src_v = pool->v;
+  c.dst_k = pool->k;
+  c.dst_v = pool->v;
+  c.src_layer_bytes = c.dst_layer_bytes = pool->layer_bytes;
+  c.block_bytes = block_bytes_of(pool);
+  c.src_ids = src_dev;
+  c.dst_ids = dst_dev;
+  c.src_blocks = c.dst_blocks = pool->num_blocks;
+  const hipError_t err = pkv::launch_block_copy(c, pool->num_layers, num_copies, stream);
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status swap_blocks(const pkv_pool* device_pool, const pkv_pool* host_pool,
+                       const int32_t* src_blocks, const int32_t* dst_blocks, int num_pairs,
+                       pkv_swap_dir direction, hipStream_t stream) {
+  if (device_pool == nullptr || host_pool == nullptr || num_pairs < 0 || num_pairs > 65535)
+    return PKV_ERR_INVALID_ARG;
+  if (direction != PKV_SWAP_OUT && direction != PKV_SWAP_IN) return PKV_ERR_INVALID_ARG;
+  const pkv_pool& d = *device_pool;
+  const pkv_pool& h = *host_pool;
+  if (d.num_layers != h.num_layers || d.num_kv_heads != h.num_kv_heads ||
+      d.head_dim != h.head_dim || d.block_size != h.block_size || d.dtype != h.dtype)
+    return PKV_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PKV_OK;
+  if (src_blocks == nullptr || dst_blocks == nullptr) return PKV_ERR_INVALID_ARG;
+  if (((uintptr_t)src_blocks & 3u) || ((uintptr_t)dst_blocks & 3u)) return PKV_ERR_ALIGNMENT;
+  if (d.num_layers > 32767) return PKV_ERR_UNSUPPORTED;
+  // The host pool must be pinned, device-mapped memory: refuse anything else instead of letting
+  // the kernel fault on it, and use the device addresses of its bases.
+  const size_t host_bytes = h.layer_bytes * (size_t)h.num_layers;
+  void* hk = nullptr;
+  void* hv = nullptr;
+  if (!pinned_device_address(h.k, host_bytes, &hk) || !pinned_device_address(h.v, host_bytes, &hv))
+    return PKV_ERR_INVALID_ARG;
+  const int32_t* src_dev = nullptr;
+  const int32_t* dst_dev = nullptr;
+  if (!device_visible(src_blocks, &src_dev) || !device_visible(dst_blocks, &dst_dev))
+    return PKV_ERR_INVALID_ARG;
+  pkv::BlockCopy c;
+  const bool out = direction == PKV_SWAP_OUT;
+  c.src_k = out ? d.k : (const char*)hk;
+  c.src_v = out ? d.v : (const char*)hv;
+  c.dst_k = out ? (char*)hk : d.k;
+  c.dst_v = out ? (char*)hv : d.v;
+  c.src_layer_bytes = out ? d.layer_bytes : h.layer_bytes;
+  c.dst_layer_bytes = out ? h.layer_bytes : d.layer_bytes;
+  c.block_bytes = block_bytes_of(&d);
+  c.src_ids = src_dev;
+  c.dst_ids = dst_dev;
+  c.src_blocks = out ? d.num_blocks : h.num_blocks;
+  c.dst_blocks = out ? h.num_blocks : d.num_blocks;
+  const hipError_t err = pkv::launch_block_copy(c, d.num_layers, num_pairs, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

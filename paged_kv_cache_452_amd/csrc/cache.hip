@@ -146,36 +146,38 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   }
 }
 
-// copy_blocks: for every pair i and layer L, the K and V regions of block src[i] (all kv heads,
-// B * D elements each) are copied to block dst[i]. One thread moves 16 bytes; the grid is
-// (16-byte chunks of a block region / 256, pairs, layers * 2 (K, V)), so consecutive workgroups
-// stream consecutive 4 KiB of one region. Pure streaming copy. (Measured: one workgroup per
-// region with 8 loads in flight per thread was 15% slower.)
-__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_pool,
-                                                         char* __restrict__ v_pool,
-                                                         size_t layer_bytes, size_t block_bytes,
-                                                         const int32_t* __restrict__ src,
-                                                         const int32_t* __restrict__ dst) {
+// Whole-block copies between two pools of one geometry: the same device pool (copy-on-write),
+// or a device pool and a pinned host pool (swapping). For pair i and layer L, the K and V regions
+// of block src[i] of the source (all kv heads, all token slots: block_bytes each) are copied to
+// block dst[i] of the destination. One thread moves 16 bytes; the grid is (16-byte chunks of a
+// region / 256, pairs, layers * 2 (K, V)), so consecutive workgroups stream consecutive 4 KiB of
+// one region. A pair with an id outside its pool is skipped. Pure streaming copy. (Measured on
+// device pools: one workgroup per region with 8 loads in flight per thread was 15% slower.)
+__global__ __launch_bounds__(256) void block_copy_kernel(BlockCopy c) {
   const size_t chunk = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (chunk * 16 >= block_bytes) return;
+  if (chunk * 16 >= c.block_bytes) return;
   const int i = blockIdx.y;
+  const int s = c.src_ids[i];
+  const int d = c.dst_ids[i];
+  if (s < 0 || s >= c.src_blocks || d < 0 || d >= c.dst_blocks) return;
   const int layer = blockIdx.z >> 1;
-  char* pool = (blockIdx.z & 1) ? v_pool : k_pool;
-  char* base = pool + (size_t)layer * layer_bytes + chunk * 16;
-  const u32x4 w = __builtin_nontemporal_load((const u32x4*)(base + (size_t)src[i] * block_bytes));
-  __builtin_nontemporal_store(w, (u32x4*)(base + (size_t)dst[i] * block_bytes));
+  const bool is_v = blockIdx.z & 1;
+  const char* src = (is_v ? c.src_v : c.src_k) + (size_t)layer * c.src_layer_bytes +
+                    (size_t)s * c.block_bytes + chunk * 16;
+  char* dst = (is_v ? c.dst_v : c.dst_k) + (size_t)layer * c.dst_layer_bytes +
+              (size_t)d * c.block_bytes + chunk * 16;
+  const u32x4 w = __builtin_nontemporal_load((const u32x4*)src);
+  __builtin_nontemporal_store(w, (u32x4*)dst);
 }
 
 }  // namespace
 
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, size_t layer_bytes, size_t block_bytes,
-                              int num_layers, const int32_t* src, const int32_t* dst,
-                              int num_copies, hipStream_t stream) {
-  if (num_copies == 0) return hipSuccess;
-  const size_t chunks = block_bytes / 16;
-  const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)num_copies, (unsigned)(2 * num_layers));
-  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, (char*)k_pool, (char*)v_pool,
-                     layer_bytes, block_bytes, src, dst);
+hipError_t launch_block_copy(const BlockCopy& c, int num_layers, int num_pairs,
+                             hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const size_t chunks = c.block_bytes / 16;
+  const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)num_pairs, (unsigned)(2 * num_layers));
+  hipLaunchKernelGGL(block_copy_kernel, grid, dim3(256), 0, stream, c);
   return hipGetLastError();
 }
 

@@ -48,9 +48,25 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         float v_inv_scale, hipStream_t stream);
 
 // Copy the K and V regions of blocks src[i] -> dst[i] in every layer (device arrays).
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, size_t layer_bytes, size_t block_bytes,
-                              int num_layers, const int32_t* src, const int32_t* dst,
-                              int num_copies, hipStream_t stream);
+// One whole-block copy launch: pair i copies block src_ids[i] of the source pool to block
+// dst_ids[i] of the destination pool, K and V of every layer. Addresses are device-visible (a
+// pinned host pool is passed by its device address).
+struct BlockCopy {
+  const char* src_k;
+  const char* src_v;
+  char* dst_k;
+  char* dst_v;
+  size_t src_layer_bytes;
+  size_t dst_layer_bytes;
+  size_t block_bytes;     // one layer's region of one block: num_kv_heads * block_size * D * elem
+  const int32_t* src_ids;
+  const int32_t* dst_ids;
+  int src_blocks;         // ids outside [0, src_blocks) / [0, dst_blocks) are skipped
+  int dst_blocks;
+};
+
+hipError_t launch_block_copy(const BlockCopy& c, int num_layers, int num_pairs,
+                             hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
                                     const int64_t* slot_mapping, int num_tokens, int num_kv_heads,

@@ -221,3 +221,27 @@ def test_fp8_pool_sizing_and_argument_errors():
     assert dec(s=0) == OK
     assert dec(nwg=32) == WORKSPACE
     assert dec(nwg=32, ws=FAKE, wsb=_ws(32) - 1) == WORKSPACE
+
+
+def test_swap_blocks_argument_errors():
+    lib = pkv.load_library()
+    each = pkv.kv_pool_bytes(2, 16, 4, 128, 16, pkv.PKV_BF16)
+    dev = pkv.kv_pool_create(FAKE, FAKE * 2, each, 2, 16, 4, 128, 16, pkv.PKV_BF16)
+    each_h = pkv.kv_pool_bytes(2, 8, 4, 128, 16, pkv.PKV_BF16)
+    host = pkv.kv_pool_create(FAKE * 3, FAKE * 4, each_h, 2, 8, 4, 128, 16, pkv.PKV_BF16)
+    other = pkv.kv_pool_create(FAKE * 3, FAKE * 4, each_h, 2, 8, 4, 64, 16, pkv.PKV_BF16)
+    fp8 = pkv.kv_pool_create(FAKE * 3, FAKE * 4, each_h, 2, 8, 4, 128, 16, pkv.PKV_FP8_E4M3)
+    f = lib.swap_blocks
+    assert f(dev._h, host._h, None, None, 0, 0, None) == OK      # nothing to copy
+    assert f(dev._h, host._h, None, None, 0, 1, None) == OK
+    assert f(None, host._h, FAKE, FAKE, 1, 0, None) == INVALID
+    assert f(dev._h, None, FAKE, FAKE, 1, 0, None) == INVALID
+    assert f(dev._h, host._h, FAKE, FAKE, 1, 2, None) == INVALID   # no such direction
+    assert f(dev._h, host._h, FAKE, FAKE, -1, 0, None) == INVALID
+    assert f(dev._h, host._h, FAKE, FAKE, 65536, 0, None) == INVALID
+    assert f(dev._h, other._h, FAKE, FAKE, 1, 0, None) == INVALID  # head_dim differs
+    assert f(dev._h, fp8._h, FAKE, FAKE, 1, 1, None) == INVALID    # element type differs
+    assert f(dev._h, host._h, None, FAKE, 1, 0, None) == INVALID
+    assert f(dev._h, host._h, FAKE + 2, FAKE, 1, 0, None) == ALIGN
+    for p in (dev, host, other, fp8):
+        p.destroy()

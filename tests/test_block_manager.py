@@ -72,38 +72,63 @@ def test_out_of_blocks_changes_nothing():
 
 def _check_invariants(m: BlockManagerModel):
     refs = [0] * m.num_blocks
+    host_refs = [0] * len(m.host_ref)
     for s, t in m.tables.items():
         assert len(t) == -(-m.tokens[s] // m.block_size)           # exactly ceil(n/B) blocks
         assert len(t) * m.block_size - m.tokens[s] <= m.block_size - 1   # waste <= B - 1
         for b in t:
-            refs[b] += 1
+            if m.is_swapped(s):
+                host_refs[b] += 1
+            else:
+                refs[b] += 1
     assert refs == m.ref                                            # counts = table references
     assert sorted(m.free) == [b for b in range(m.num_blocks) if refs[b] == 0]
+    assert host_refs == m.host_ref
+    assert sorted(m.host_free) == [b for b in range(len(host_refs)) if host_refs[b] == 0]
 
 
-def _random_ops(seed, n_ops=400, num_blocks=64, block_size=4):
+def _random_ops(seed, n_ops=400, num_blocks=64, block_size=4, swaps=False):
+    """A seeded operation sequence. With swaps, the generator keeps its own guess of which
+    sequences are swapped out (a refused operation can make it wrong; _live filters those)."""
     rng = random.Random(seed)
     ops, live, nxt = [], [], 0
+    out = set()
     for _ in range(n_ops):
         r = rng.random()
-        if r < 0.15 or not live:
+        dev = [s for s in live if s not in out]
+        if r < 0.15 or not dev:
             ops.append(("allocate", nxt, rng.randint(0, 3 * block_size))); live.append(nxt); nxt += 1
         elif r < 0.25:
-            ops.append(("fork", rng.choice(live), nxt)); live.append(nxt); nxt += 1
+            ops.append(("fork", rng.choice(dev), nxt)); live.append(nxt); nxt += 1
         elif r < 0.35:
-            s = rng.choice(live); ops.append(("release", s)); live.remove(s)
+            s = rng.choice(live); ops.append(("release", s)); live.remove(s); out.discard(s)
+        elif swaps and r < 0.43:
+            group = rng.sample(dev, min(len(dev), rng.randint(1, 3)))
+            ops.append(("swap_out", group)); out.update(group)
+        elif swaps and r < 0.51 and out:
+            group = rng.sample(sorted(out), min(len(out), rng.randint(1, 3)))
+            ops.append(("swap_in", group)); out.difference_update(group)
         else:
-            ops.append(("append", [rng.choice(live) for _ in range(rng.randint(1, 4))]))
+            ops.append(("append", [rng.choice(dev) for _ in range(rng.randint(1, 4))]))
     return ops
 
 
 def _live(m, op):
-    """False when the op names a sequence an earlier failed operation never created."""
+    """False when the op names a sequence an earlier failed operation never created, or one on
+    the wrong side of a swap for it (both implementations refuse those; tested separately)."""
     if op[0] == "allocate":
         return True
-    if op[0] in ("fork", "release"):
+    if op[0] == "release":
         return op[1] in m.tables
-    return all(s in m.tables for s in op[1])
+    if op[0] == "fork":
+        return op[1] in m.tables and not m.is_swapped(op[1])
+    if not all(s in m.tables for s in op[1]):
+        return False
+    if op[0] == "swap_out":
+        return not any(m.is_swapped(s) for s in op[1])
+    if op[0] == "swap_in":
+        return all(m.is_swapped(s) for s in op[1])
+    return not any(m.is_swapped(s) for s in op[1])
 
 
 def _apply(m, op):
@@ -116,13 +141,17 @@ def _apply(m, op):
         return m.fork(op[1], op[2])
     if kind == "release":
         return m.release(op[1])
+    if kind == "swap_out":
+        return m.swap_out(op[1])
+    if kind == "swap_in":
+        return m.swap_in(op[1])
     return m.append_batch(op[1])
 
 
 @pytest.mark.parametrize("seed", range(6))
 def test_model_invariants_under_random_operations(seed):
-    m = BlockManagerModel(64, 4)
-    for op in _random_ops(seed):
+    m = BlockManagerModel(64, 4, num_host_blocks=40)
+    for op in _random_ops(seed, swaps=True):
         try:
             _apply(m, op)
         except OutOfBlocks:
@@ -136,11 +165,12 @@ def test_copy_on_write_never_changes_what_other_sequences_read(seed):
     exactly its own token history (what the device pool must hold after reshape_and_cache and
     copy_blocks)."""
     B = 4
-    m = BlockManagerModel(64, B)
+    m = BlockManagerModel(64, B, num_host_blocks=40)
     pool = {}            # slot -> token id
+    host = {}            # host slot -> token id
     history = {}         # seq -> token ids
     tok = 1000
-    for op in _random_ops(seed):
+    for op in _random_ops(seed, swaps=True):
         if not _live(m, op):
             continue
         try:
@@ -156,6 +186,16 @@ def test_copy_on_write_never_changes_what_other_sequences_read(seed):
             elif op[0] == "release":
                 m.release(op[1])
                 del history[op[1]]
+            elif op[0] in ("swap_out", "swap_in"):
+                out = op[0] == "swap_out"
+                pairs = m.swap_out(op[1]) if out else m.swap_in(op[1])
+                src_pool, dst_pool = (pool, host) if out else (host, pool)
+                for src, dst in pairs:          # whole-block copies, every slot
+                    for i in range(B):
+                        if src * B + i in src_pool:
+                            dst_pool[dst * B + i] = src_pool[src * B + i]
+                        else:
+                            dst_pool.pop(dst * B + i, None)
             else:
                 slots, copies = m.append_batch(op[1])
                 for src, dst in copies:         # device copies happen before the token writes
@@ -170,7 +210,55 @@ def test_copy_on_write_never_changes_what_other_sequences_read(seed):
             continue
         for s, h in history.items():
             t = m.table(s)
-            assert [pool[t[i // B] * B + i % B] for i in range(len(h))] == h
+            where = host if m.is_swapped(s) else pool
+            assert [where[t[i // B] * B + i % B] for i in range(len(h))] == h
+
+
+def test_swap_worked_example():
+    """Derived by hand from the swap rules: a sequence and its fork, whose last blocks differ
+    after copy-on-write, are preempted together and resumed in the other order."""
+    m = BlockManagerModel(10, 4, num_host_blocks=6)
+    m.allocate(1, 9)                       # 3 blocks: [0, 1, 2], block 2 holds 1 token
+    m.fork(1, 2)
+    assert m.append(2) == (3 * 4 + 1, (2, 3))    # writes into shared block 2: copy to 3
+    # out: distinct blocks in order 0, 1, 2 (seq 1), 3 (seq 2) -> host blocks 0, 1, 2, 3;
+    # device blocks reach zero references in the order 2 (seq 1's last), 0, 1, 3 (seq 2)
+    assert m.swap_out([1, 2]) == [(0, 0), (1, 1), (2, 2), (3, 3)]
+    assert m.table(1) == [0, 1, 2] and m.table(2) == [0, 1, 3]       # host ids now
+    assert m.host_ref[:4] == [2, 2, 1, 1] and m.host_free == [4, 5]
+    assert m.free == [4, 5, 6, 7, 8, 9, 2, 0, 1, 3]
+    # in, seq 2 first: host blocks in order 0, 1, 3, 2 take device blocks 4, 5, 6, 7
+    assert m.swap_in([2, 1]) == [(0, 4), (1, 5), (3, 6), (2, 7)]
+    assert m.table(1) == [4, 5, 7] and m.table(2) == [4, 5, 6]
+    assert m.ref[4:8] == [2, 2, 1, 1]                                 # sharing survived
+    assert m.free == [8, 9, 2, 0, 1, 3] and m.host_free == [4, 5, 3, 0, 1, 2]
+    assert m.num_tokens(1) == 9 and m.num_tokens(2) == 10
+
+
+def test_swap_refusals_change_nothing():
+    m = BlockManagerModel(6, 4, num_host_blocks=2)
+    m.allocate(0, 12)                      # 3 blocks
+    m.allocate(1, 4)
+    before = (list(m.free), list(m.ref), list(m.host_free), m.table(0))
+    with pytest.raises(OutOfBlocks):
+        m.swap_out([0])                    # 3 blocks, 2 host blocks
+    with pytest.raises(KeyError):
+        m.swap_out([1, 1])
+    with pytest.raises(KeyError):
+        m.swap_in([1])                     # not swapped out
+    assert (list(m.free), list(m.ref), list(m.host_free), m.table(0)) == before
+    m.swap_out([1])
+    with pytest.raises(KeyError):
+        m.append(1)
+    with pytest.raises(KeyError):
+        m.fork(1, 7)
+    assert m.free == [4, 5, 3] and m.host_free == [1]
+    m.allocate(2, 12)                      # takes blocks 4, 5 and the freed block 3
+    with pytest.raises(OutOfBlocks):
+        m.swap_in([1])                     # no device block left
+    assert m.is_swapped(1) and m.host_free == [1]
+    m.release(1)                           # a swapped-out sequence frees its host block
+    assert m.host_free == [1, 0] and 1 not in m.tables
 
 
 # ---- the library's native block manager against the model (host code, no GPU needed) ----
@@ -205,6 +293,10 @@ def _native_apply(bm, op):
         return bm.fork(op[1], op[2])
     if kind == "release":
         return bm.release(op[1])
+    if kind == "swap_out":
+        return bm.swap_out(op[1])
+    if kind == "swap_in":
+        return bm.swap_in(op[1])
     return bm.append(op[1])
 
 
@@ -213,9 +305,9 @@ def _native_apply(bm, op):
 def test_native_matches_model_on_random_operations(seed, block_size):
     """Same operations on both: identical slots, copies, tables, lengths, free counts and
     refusals."""
-    m = BlockManagerModel(64, block_size)
-    bm = pkv.BlockManager(64, block_size)
-    for op in _random_ops(seed + 100 * block_size, block_size=block_size):
+    m = BlockManagerModel(64, block_size, num_host_blocks=40)
+    bm = pkv.BlockManager(64, block_size, num_host_blocks=40)
+    for op in _random_ops(seed + 100 * block_size, block_size=block_size, swaps=True):
         if not _live(m, op):
             continue
         try:
@@ -232,8 +324,10 @@ def test_native_matches_model_on_random_operations(seed, block_size):
         if op[0] == "append" and want_err is None:
             assert got[0].tolist() == want[0], op
             assert [tuple(c) for c in got[1].tolist()] == want[1], op
-        assert bm.num_free == m.num_free()
-        seqs = sorted(m.tables)
+        if op[0].startswith("swap") and want_err is None:
+            assert [tuple(c) for c in got.tolist()] == want, op
+        assert bm.num_free == m.num_free() and bm.num_free_host == m.num_free_host()
+        seqs = sorted(s for s in m.tables if not m.is_swapped(s))
         if seqs:
             mb = max(1, max(len(t) for t in m.tables.values()))
             bt, cl = bm.tables(seqs, mb)
@@ -259,3 +353,33 @@ def test_native_argument_errors():
     lib = pkv.load_library()
     assert lib.kv_block_manager_num_free(None) == -1
     lib.kv_block_manager_destroy(None)
+
+
+def test_native_swap_argument_errors():
+    import ctypes
+    bm = pkv.BlockManager(8, 4, num_host_blocks=2)
+    bm.allocate(1, 5)                      # 2 blocks
+    bm.allocate(2, 4)                      # 1 block
+    for fn, args in [(bm.swap_out, ([1, 1],)), (bm.swap_out, ([9],)), (bm.swap_in, ([1],))]:
+        with pytest.raises(pkv.PagedKVError) as e:
+            fn(*args)
+        assert e.value.status == -1
+    with pytest.raises(pkv.PagedKVError) as e:
+        bm.swap_out([1, 2])                # 3 blocks, 2 host blocks
+    assert e.value.status == pkv.PKV_ERR_NO_BLOCKS
+    lib = pkv.load_library()
+    ids = (ctypes.c_int64 * 1)(1)
+    src, dst, k = (ctypes.c_int32 * 4)(), (ctypes.c_int32 * 4)(), ctypes.c_int(-1)
+    assert lib.kv_block_manager_swap_out(bm._h, ids, 1, src, dst, 1, ctypes.byref(k)) == -1
+    assert k.value == 0                    # capacity 1 < 2 pairs: refused, nothing moved
+    assert bm.num_free == 5 and bm.num_free_host == 2
+    assert bm.swap_out([1]).tolist() == [[0, 0], [1, 1]]
+    for fn, args in [(bm.append, ([1],)), (bm.fork, (1, 5)), (bm.tables, ([1], 4))]:
+        with pytest.raises(pkv.PagedKVError) as e:
+            fn(*args)
+        assert e.value.status == -1
+    assert bm.swap_in([1]).tolist() == [[0, 3], [1, 4]]
+    bt, cl = bm.tables([1], 4)
+    assert bt[0].tolist() == [3, 4, -1, -1] and cl.tolist() == [5]
+    assert lib.kv_block_manager_num_free_host(None) == -1
+    assert lib.kv_block_manager_swap_in(None, ids, 1, src, dst, 4, ctypes.byref(k)) == -1
