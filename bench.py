@@ -46,12 +46,13 @@ def measured_traffic(workload: str):
     on the current kernel source and this workload."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            recs = json.load(f).get("records", [])
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("decode_source_sha256_16") != source_hash() or rec.get("workload") != workload:
-        return None
-    return rec.get("bytes_per_launch")
+    for rec in recs:
+        if rec.get("decode_source_sha256_16") == source_hash() and rec.get("workload") == workload:
+            return rec.get("bytes_per_launch")
+    return None
 
 
 def cpu_baseline(batch, spec, layers, budget_s=15.0, kv_scales=None):
