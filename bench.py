@@ -25,12 +25,18 @@ DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_452_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
-def algorithmic_bytes(lens, num_q_heads, num_kv_heads, head_dim, elem=2, block=16, kv_elem=None):
+def algorithmic_bytes(lens, num_q_heads, num_kv_heads, head_dim, elem=2, block=16, kv_elem=None,
+                      fused=False):
     """Bytes one decode launch must move: every cached K and V row of every sequence once per kv
     head, q in, out back, the used block-table entries and the context lengths. elem: bytes of a
-    q/out element; kv_elem: bytes of a pool element (default elem; 1 for fp8 pools)."""
+    q/out element; kv_elem: bytes of a pool element (default elem; 1 for fp8 pools). fused: the
+    launch also appends each sequence's newest token (its K/V rows read from the step's input
+    instead of the pool, and written into the pool)."""
     kv_elem = elem if kv_elem is None else kv_elem
     kv = sum(int(n) for n in lens) * num_kv_heads * head_dim * kv_elem * 2
+    if fused:
+        new = sum(1 for n in lens if int(n) > 0) * num_kv_heads * head_dim * 2
+        kv += new * (elem - kv_elem) + new * kv_elem   # input rows instead of pool rows, + write
     qo = len(lens) * num_q_heads * head_dim * elem * 2
     tables = sum(-(-int(n) // block) for n in lens) * 4
     return kv + qo + tables + 4 * len(lens)
@@ -283,6 +289,9 @@ def main() -> int:
     ap.add_argument("--kv-dtype", choices=["model", "fp8"], default="model",
                     help="pool element type: the model's 16-bit type (default) or E4M3 codes "
                          "with one scale per pool")
+    ap.add_argument("--fused", action="store_true",
+                    help="run each layer's step as one paged_attention_decode_append launch "
+                         "instead of reshape_and_cache followed by paged_attention_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel", choices=["decode", "copy_blocks", "swap"], default="decode",
                     help="decode (the hot path, default), copy_blocks (copy-on-write copies) or "
@@ -348,14 +357,26 @@ def main() -> int:
                                        batch.context_lens, spec.scale, Hq, Hkv, D, B, max_ctx,
                                        nwg, ws, stream)
 
+    def fused(i, k, v):
+        pkv.paged_attention_decode_append(outs[i], batch.q, batch.new_key, batch.new_value, k, v,
+                                          batch.block_tables, batch.context_lens, spec.scale, Hq,
+                                          Hkv, D, B, max_ctx, nwg, ws, stream,
+                                          kv_scales=(ks, vs) if fp8 else None)
+
     def step():
         for i, (k, v) in enumerate(layers):
-            cache(k, v)
-            decode(i, k, v)
+            if not args.fused:
+                cache(k, v)
+                decode(i, k, v)
+            else:
+                fused(i, k, v)
 
     def sweep_decode():
         for i, (k, v) in enumerate(layers):
-            decode(i, k, v)
+            if not args.fused:
+                decode(i, k, v)
+            else:
+                fused(i, k, v)
 
     def timed(fn, reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -378,11 +399,13 @@ def main() -> int:
     ms_total = timed(step, args.steps)
     ms_step = ms_total / args.steps
 
-    per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=1 if fp8 else 2)
+    per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=1 if fp8 else 2,
+                                   fused=args.fused)
     value = per_launch * L / (ms_step * 1e-3) / 1e9
     achieved = per_launch / (avg_decode_ms * 1e-3) / 1e9
     workload = ((spec.name if args.layers <= 0 else f"{spec.name}, {L} layers") +
-                ("" if B == 16 else f", block size {B}") + (", fp8 E4M3 KV" if fp8 else ""))
+                ("" if B == 16 else f", block size {B}") + (", fp8 E4M3 KV" if fp8 else "") +
+                (", fused step" if args.fused else ""))
     traffic = measured_traffic(workload)
     grid = nwg or pkv.paged_attention_num_workgroups(S, Hq, Hkv, max_ctx, B)
     rec = {
@@ -403,20 +426,24 @@ def main() -> int:
                    "head_dim": D, "block_size": B, "num_layers": L,
                    "num_blocks_per_layer": t.num_blocks, "decode_workgroups": grid,
                    "kv_dtype": "fp8 e4m3, one scale per pool" if fp8 else spec.dtype,
-                   "step": "per layer: reshape_and_cache of the step's new tokens + "
-                           "paged_attention_decode"},
+                   "step": ("per layer: reshape_and_cache of the step's new tokens, then "
+                            "paged_attention_decode" if not args.fused else
+                            "per layer: one paged_attention_decode_append launch (the step's new "
+                            "tokens appended to the pool and attended to with the cached "
+                            "context)")},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_per_layer_step": round(S * L / (ms_step * 1e-3), 1),
         "decode_launch_us": round(avg_decode_ms * 1e3, 2),
-        "timing": "roofline.achieved: back-to-back decode launches over all layers between two "
-                  "HIP events on the launch stream (mean launch duration), timed first; value: K "
-                  "whole steps between two HIP events",
+        "timing": "roofline.achieved: back-to-back step launches of the decode kernel over all "
+                  "layers between two HIP events on the launch stream (mean launch duration), "
+                  "timed first; value: K whole steps between two HIP events",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": per_launch,
-                     "kernel": "paged_attention_decode (one persistent decode kernel; split "
-                               "streams merged in it)"},
+                     "kernel": ("paged_attention_decode" if not args.fused else
+                                "paged_attention_decode_append") +
+                               " (one persistent decode kernel; split streams merged in it)"},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(batch, spec, range(L), kv_scales=(ks, vs) if fp8

@@ -381,6 +381,46 @@ pkv_status paged_attention_decode_fp8(void* out, const void* q, const void* k_po
                                       int num_workgroups, pkv_dtype dtype, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * One decode step fused into one launch: the same result as reshape_and_cache of each sequence's
+ * newest token followed by paged_attention_decode ("PagedAttention and KV Cache Management"
+ * (blog.sejan.dev), section "How Block Paging Operates During Generation": each step appends one
+ * token per sequence, then attends over the whole context).
+ *   key, value   device, [num_seqs][num_kv_heads][head_dim] of dtype: row s is the K / V of
+ *                sequence s's token at position context_lens[s] - 1, the step's new token.
+ *                Ignored for sequences with context length 0.
+ *   k_pool, v_pool  one layer's sub-pools; the new token is written into its slot
+ *                (block_tables[s][(n - 1) / block_size] * block_size + (n - 1) % block_size,
+ *                bit-exact as reshape_and_cache writes it) by the workgroup that reads that
+ *                slot's tile, before it reads anything, and then attended to like every other
+ *                cached token.
+ * context_lens and max_context_len count the new token. Everything else (layout, workspace,
+ * errors, block-table trust) as paged_attention_decode. No other sequence may read or share the
+ * blocks written here (copy-on-write has already made them private).
+ */
+pkv_status paged_attention_decode_append(void* out, const void* q, const void* key,
+                                         const void* value, void* k_pool, void* v_pool,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         float scale, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, int num_seqs,
+                                         int max_blocks_per_seq, int max_context_len,
+                                         int num_workgroups, pkv_dtype dtype, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
+/* paged_attention_decode_append over fp8 pools: the new token is quantized as
+ * reshape_and_cache_fp8 does (k_scale, v_scale), written into the pool, and attended to through
+ * the values of its codes, as paged_attention_decode_fp8 would read them back. */
+pkv_status paged_attention_decode_append_fp8(void* out, const void* q, const void* key,
+                                             const void* value, void* k_pool, void* v_pool,
+                                             const int32_t* block_tables,
+                                             const int32_t* context_lens, float scale,
+                                             float k_scale, float v_scale, int num_q_heads,
+                                             int num_kv_heads, int head_dim, int block_size,
+                                             int num_seqs, int max_blocks_per_seq,
+                                             int max_context_len, int num_workgroups,
+                                             pkv_dtype dtype, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(pkv_status status);
 

@@ -25,6 +25,7 @@ EXPORTED = ("kv_pool_bytes", "kv_pool_create", "kv_pool_layer", "kv_pool_destroy
             "reshape_and_cache", "paged_attention_num_workgroups",
             "paged_attention_workspace_bytes", "paged_attention_decode", "copy_blocks",
             "reshape_and_cache_fp8", "paged_attention_decode_fp8", "swap_blocks",
+            "paged_attention_decode_append", "paged_attention_decode_append_fp8",
             "kv_block_manager_create", "kv_block_manager_destroy", "kv_block_manager_num_free",
             "kv_block_manager_allocate", "kv_block_manager_fork", "kv_block_manager_append",
             "kv_block_manager_release", "kv_block_manager_tables", "kv_block_manager_num_free_host",
@@ -76,6 +77,12 @@ def load_library(build_if_missing: bool = True):
     lib.paged_attention_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, f, f, f, i, i, i, i, i, i,
                                                i, i, i, vp, sz, vp]
     lib.paged_attention_decode_fp8.restype = i
+    lib.paged_attention_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f, i, i, i, i, i,
+                                                  i, i, i, i, vp, sz, vp]
+    lib.paged_attention_decode_append.restype = i
+    lib.paged_attention_decode_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f, f, f, i,
+                                                      i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.paged_attention_decode_append_fp8.restype = i
     lib.copy_blocks.argtypes = [vp, vp, vp, i, vp]
     lib.swap_blocks.argtypes = [vp, vp, vp, vp, i, i, vp]
     lib.swap_blocks.restype = i
@@ -303,6 +310,36 @@ def swap_blocks(device_pool: "KVPool", host_pool: "KVPool", src_blocks, dst_bloc
     _check("swap_blocks", load_library().swap_blocks(device_pool._h, host_pool._h,
                                                      _ptr(src_blocks), _ptr(dst_blocks), n,
                                                      int(direction), _stream(stream)))
+
+
+def paged_attention_decode_append(out, q, key, value, k_pool, v_pool, block_tables, context_lens,
+                                  scale: float, num_q_heads: int, num_kv_heads: int,
+                                  head_dim: int, block_size: int, max_context_len: int,
+                                  num_workgroups: int = 0, workspace=None, stream=None,
+                                  kv_scales=None) -> None:
+    """One fused decode step: each sequence's newest token (key/value [S][Hkv][D], at position
+    context_lens[s] - 1) is written into the pool and attended to with the rest of the context.
+    kv_scales=(k_scale, v_scale) for fp8 pools."""
+    _require_cuda(out, q, key, value, k_pool, v_pool, block_tables, context_lens, workspace)
+    S = q.shape[0]
+    max_blocks = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    if kv_scales is None:
+        rc = lib.paged_attention_decode_append(
+            _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool),
+            _ptr(block_tables), _ptr(context_lens), float(scale), num_q_heads, num_kv_heads,
+            head_dim, block_size, S, max_blocks, max_context_len, num_workgroups,
+            _dtype_code(q), _ptr(workspace), ws_bytes, _stream(stream))
+        _check("paged_attention_decode_append", rc)
+    else:
+        rc = lib.paged_attention_decode_append_fp8(
+            _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool),
+            _ptr(block_tables), _ptr(context_lens), float(scale), float(kv_scales[0]),
+            float(kv_scales[1]), num_q_heads, num_kv_heads, head_dim, block_size, S, max_blocks,
+            max_context_len, num_workgroups, _dtype_code(q), _ptr(workspace), ws_bytes,
+            _stream(stream))
+        _check("paged_attention_decode_append_fp8", rc)
 
 
 def copy_blocks(pool: "KVPool", src_blocks, dst_blocks, stream=None) -> None:

@@ -343,7 +343,10 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
 
 namespace {
 
-pkv_status decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+// Decode, plain or fused with the append of each sequence's newest token (new_k / new_v non-null:
+// rows [num_seqs][num_kv_heads][head_dim] of q's element type).
+pkv_status decode_impl(void* out, const void* q, const void* new_k, const void* new_v,
+                       const void* k_pool, const void* v_pool,
                        const int32_t* block_tables, const int32_t* context_lens, float scale,
                        bool kv_fp8, float k_scale, float v_scale, int num_q_heads,
                        int num_kv_heads, int head_dim, int block_size, int num_seqs,
@@ -368,8 +371,11 @@ pkv_status decode_impl(void* out, const void* q, const void* k_pool, const void*
     return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
+  const bool append = new_k != nullptr || new_v != nullptr;
+  if (append && (new_k == nullptr || new_v == nullptr)) return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
-      ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u))
+      ((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+      (append && (!aligned16(new_k) || !aligned16(new_v))))
     return PKV_ERR_ALIGNMENT;
 
   const int grid = resolve_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len,
@@ -401,8 +407,13 @@ pkv_status decode_impl(void* out, const void* q, const void* k_pool, const void*
   a.max_blocks = max_blocks_per_seq;
   a.max_tokens = max_blocks_per_seq * block_size;
   a.sub_shift = block_size == 32 ? 1 : 0;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  const float one = 1.0f;
+  a.k_inv = one / k_scale;
+  a.v_inv = one / v_scale;
   const hipError_t err =
-      pkv::launch_decode(a, grid, head_dim, dtype == PKV_BF16, kv_fp8, stream);
+      pkv::launch_decode(a, grid, head_dim, dtype == PKV_BF16, kv_fp8, append, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -416,8 +427,40 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
                                   int block_size, int num_seqs, int max_blocks_per_seq,
                                   int max_context_len, int num_workgroups, pkv_dtype dtype,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, scale, false, 1.0f, 1.0f,
-                     num_q_heads, num_kv_heads, head_dim, block_size, num_seqs,
+  return decode_impl(out, q, nullptr, nullptr, k_pool, v_pool, block_tables, context_lens, scale,
+                     false, 1.0f, 1.0f, num_q_heads, num_kv_heads, head_dim, block_size, num_seqs,
+                     max_blocks_per_seq, max_context_len, num_workgroups, dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+pkv_status paged_attention_decode_append(void* out, const void* q, const void* key,
+                                         const void* value, void* k_pool, void* v_pool,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         float scale, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, int num_seqs,
+                                         int max_blocks_per_seq, int max_context_len,
+                                         int num_workgroups, pkv_dtype dtype, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs > 0 && (key == nullptr || value == nullptr)) return PKV_ERR_INVALID_ARG;
+  return decode_impl(out, q, key, value, k_pool, v_pool, block_tables, context_lens, scale, false,
+                     1.0f, 1.0f, num_q_heads, num_kv_heads, head_dim, block_size, num_seqs,
+                     max_blocks_per_seq, max_context_len, num_workgroups, dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+pkv_status paged_attention_decode_append_fp8(void* out, const void* q, const void* key,
+                                             const void* value, void* k_pool, void* v_pool,
+                                             const int32_t* block_tables,
+                                             const int32_t* context_lens, float scale,
+                                             float k_scale, float v_scale, int num_q_heads,
+                                             int num_kv_heads, int head_dim, int block_size,
+                                             int num_seqs, int max_blocks_per_seq,
+                                             int max_context_len, int num_workgroups,
+                                             pkv_dtype dtype, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs > 0 && (key == nullptr || value == nullptr)) return PKV_ERR_INVALID_ARG;
+  return decode_impl(out, q, key, value, k_pool, v_pool, block_tables, context_lens, scale, true,
+                     k_scale, v_scale, num_q_heads, num_kv_heads, head_dim, block_size, num_seqs,
                      max_blocks_per_seq, max_context_len, num_workgroups, dtype, workspace,
                      workspace_bytes, stream);
 }
@@ -430,8 +473,8 @@ pkv_status paged_attention_decode_fp8(void* out, const void* q, const void* k_po
                                       int max_blocks_per_seq, int max_context_len,
                                       int num_workgroups, pkv_dtype dtype, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream) {
-  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, scale, true, k_scale,
-                     v_scale, num_q_heads, num_kv_heads, head_dim, block_size, num_seqs,
+  return decode_impl(out, q, nullptr, nullptr, k_pool, v_pool, block_tables, context_lens, scale,
+                     true, k_scale, v_scale, num_q_heads, num_kv_heads, head_dim, block_size, num_seqs,
                      max_blocks_per_seq, max_context_len, num_workgroups, dtype, workspace,
                      workspace_bytes, stream);
 }

@@ -54,41 +54,6 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
-// OCP E4M3 code of an fp32 value: round to nearest even, saturating at +-448, NaN kept (with its
-// sign), sign kept for zero. Integer arithmetic on the fp32 bits, so every device gives the same
-// code.
-__device__ __forceinline__ unsigned e4m3_code(float y) {
-  const unsigned bits = __float_as_uint(y);
-  const unsigned sign = (bits >> 24) & 0x80u;
-  const unsigned a = bits & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;  // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu; // |y| >= 448 (and infinity): saturate
-  const int e = (int)(a >> 23) - 127;        // exponent of |y| (fp32 denormals: -127)
-  if (e < -6) {
-    // Below the smallest normal 2^-6: code = |y| * 2^9 rounded, i.e. the 24-bit significand
-    // shifted right by 14 - e bits (a result of 8 is the smallest normal, code 0x08).
-    const int sh = 14 - e;
-    if (sh >= 32) return sign;
-    const unsigned sig = (a & 0x7FFFFFu) | 0x800000u;
-    unsigned q = sig >> sh;
-    const unsigned rem = sig & ((1u << sh) - 1u);
-    const unsigned half = 1u << (sh - 1);
-    q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
-    return sign | q;
-  }
-  // Normal: 3 mantissa bits from 23, exponent field e + 7.
-  const unsigned m = a & 0x7FFFFFu;
-  unsigned q = m >> 20;
-  const unsigned rem = m & 0xFFFFFu;
-  q += (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
-  unsigned ef = (unsigned)(e + 7);
-  if (q == 8u) {
-    q = 0u;
-    ++ef;
-  }
-  return sign | (ef << 3) | q;
-}
-
 // reshape_and_cache into fp8 pools: one thread quantizes eight consecutive dims of one (token,
 // kv head): K is one 8-byte store (the fp8 K tile keeps those eight dims contiguous), V eight
 // byte stores (the fp8 V tile keeps four consecutive tokens of a dim together).

@@ -64,8 +64,9 @@ constexpr int kQRows = 64;
 constexpr int kMergeRound = 8;
 
 // Tile buffers per wavefront (blocks in flight = kRing - 1), sized to stay within 256 VGPRs so
-// two workgroups fit on each compute unit. 64 (the tile-id window) is a multiple of both.
-template <int D>
+// two workgroups fit on each compute unit. (fp8 tiles hold half the bytes, but a deeper ring for
+// them does not fit: 5 or 6 slots at d128 spill.)
+template <int D, bool KV8, bool APPEND>
 constexpr int kRing = D == 128 ? 4 : 8;
 
 template <bool BF16>
@@ -94,6 +95,9 @@ struct Elem<true> {
   }
   static __device__ __forceinline__ unsigned short store(float x) {
     return __builtin_bit_cast(unsigned short, (__bf16)x);
+  }
+  static __device__ __forceinline__ float widen(unsigned short b) {
+    return __uint_as_float((unsigned)b << 16);
   }
   // Four E4M3 codes (bytes 0..3 of w) -> four bf16 in two dwords (exact: E4M3 is a subset).
   static __device__ __forceinline__ u32x2 from_fp8(unsigned w) {
@@ -125,6 +129,9 @@ struct Elem<false> {
   }
   static __device__ __forceinline__ unsigned short store(float x) {
     return __builtin_bit_cast(unsigned short, (_Float16)x);
+  }
+  static __device__ __forceinline__ float widen(unsigned short b) {
+    return (float)__builtin_bit_cast(_Float16, b);
   }
   // Four E4M3 codes -> four fp16 (exact: every E4M3 value is an fp16 value).
   static __device__ __forceinline__ u32x2 from_fp8(unsigned w) {
@@ -160,7 +167,7 @@ __device__ __forceinline__ int range_owner(int p, int nwg, int W) {
   return (int)(((long)(p + 1) * nwg - 1) / W);
 }
 
-template <int D, bool BF16, bool KV8, int RING>
+template <int D, bool BF16, bool KV8, bool APPEND, int RING>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void
 paged_decode_kernel(DecodeLaunch a) {
   using E = Elem<BF16>;
@@ -176,7 +183,8 @@ paged_decode_kernel(DecodeLaunch a) {
   constexpr int kDims = D / kLanesPerHead;                // 8 (d128) or 4 (d64)
   constexpr int kChunks = D / 8;                          // 16-byte chunks per q row
   constexpr int kQLoads = kQRows * kChunks / kThreads;
-  static_assert(64 % RING == 0, "tile-id windows must hold whole ring turns");
+  // A load RING - 1 blocks ahead reads its tile id from the current or the next 64-id window.
+  static_assert(RING >= 2 && RING <= 64, "prefetch must stay within the next tile-id window");
 
   __shared__ int s_ps[kMaxSeqs + 1];  // s_ps[s] = blocks of sequences 0..s-1
   __shared__ int s_len[kMaxSeqs];     // context lengths (clamped to the table row)
@@ -350,8 +358,65 @@ paged_decode_kernel(DecodeLaunch a) {
   };
   unsigned win_a = window(0);
   unsigned win_b = mw > 64 ? window(1) : 0u;
-  wait_vmem();
-  __syncthreads();  // staged q visible to every wave
+  if constexpr (APPEND) {
+    // The step's new token of every stream whose last unit lies in this range goes into the pool
+    // here, before any tile is read: the workgroup that reads that unit writes it itself (head
+    // tiles of one kv head write the same bytes), so the main loop reads it like any other token.
+    // Wave w takes the w-th, (w+4)-th, ... such stream; lane l writes dims 2l and 2l + 1.
+    Stream t = cur;
+    int k = 0;
+    while (t.start < r1) {
+      if (t.end <= r1 && k++ % kWaves == wave) {
+        const int g = t.gh / a.head_tiles;
+        const int p = t.n - 1;  // the new token's position
+        const size_t row = (((size_t)t.s * a.num_kv_heads + g) * D) / 2 + lane;
+        const bool has = lane < D / 2;
+        const unsigned kw = has ? ((const unsigned*)a.new_k)[row] : 0u;
+        const unsigned vw = has ? ((const unsigned*)a.new_v)[row] : 0u;
+        const unsigned b =
+            (unsigned)a.block_tables[(size_t)t.s * a.max_blocks + (p >> (4 + a.sub_shift))];
+        wait_vmem();
+        if (has) {
+          const int tt = p & 15;
+          const int d = 2 * lane;
+          const size_t tile =
+              ((size_t)((b * (unsigned)a.num_kv_heads + (unsigned)g) << a.sub_shift) +
+               (size_t)((p >> 4) & ((1 << a.sub_shift) - 1))) * (kBlock * D);
+          if constexpr (KV8) {  // quantized as reshape_and_cache_fp8 does
+            const unsigned kc = e4m3_code(E::widen((unsigned short)kw) * a.k_inv) |
+                                e4m3_code(E::widen((unsigned short)(kw >> 16)) * a.k_inv) << 8;
+            const unsigned vc = e4m3_code(E::widen((unsigned short)vw) * a.v_inv) |
+                                e4m3_code(E::widen((unsigned short)(vw >> 16)) * a.v_inv) << 8;
+            unsigned char* kp = (unsigned char*)a.k_pool + tile;
+            unsigned char* vp = (unsigned char*)a.v_pool + tile;
+            // K8 [d/64][(d/8)%4][token][(d/32)%2][d%8]: dims d, d + 1 are adjacent bytes
+            *(unsigned short*)(kp + (size_t)(d / 64) * 1024 + (size_t)(16 * ((d / 8) % 4) + tt) * 16 +
+                               ((d / 32) % 2) * 8 + d % 8) = (unsigned short)kc;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {  // V8 [d/64][token/4][d%16][(d/16)%4][token%4]
+              const int de = d + e;
+              vp[(size_t)(de / 64) * 1024 + (size_t)((tt / 4) * 16 + de % 16) * 16 +
+                 ((de / 16) % 4) * 4 + tt % 4] = (unsigned char)(vc >> (8 * e));
+            }
+          } else {
+            unsigned short* kp = (unsigned short*)a.k_pool + tile;
+            unsigned short* vp = (unsigned short*)a.v_pool + tile;
+            // K [d/8][token][d%8]: dims d, d + 1 are one dword
+            *(unsigned*)(kp + (size_t)(d / 8) * 128 + (size_t)tt * 8 + d % 8) = kw;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {  // V [d/32][token/4][d%16][(d/16)%2][token%4]
+              const int de = d + e;
+              vp[((((size_t)(de / 32) * 4 + tt / 4) * 16 + de % 16) * 2 + (de / 16) % 2) * 4 +
+                 tt % 4] = (unsigned short)(vw >> (16 * e));
+            }
+          }
+        }
+      }
+      t = stream_after(t);
+    }
+  }
+  wait_vmem();      // the windows (and the new tokens' stores) are complete
+  __syncthreads();  // staged q and the new tokens visible to every wave
   int chunk_a = 0;
   auto tile_of = [&](int m) -> unsigned {
     const unsigned w = (m >> 6) == chunk_a ? win_a : win_b;
@@ -402,8 +467,9 @@ paged_decode_kernel(DecodeLaunch a) {
   };
 
   // Split streams of this range: 0 = the one holding r0, 1 = the one holding r1 - 1.
-  Stream split0, split1;
-  bool has0 = false, has1 = false;
+  // Only their start positions stay live through the main loop (scalar registers are the scarce
+  // resource there); the merge rebuilds the streams from them. -1: no such stream.
+  int split0 = -1, split1 = -1;
 
   // ---- End of a stream: combine the four waves, then store it or leave its partial. ----
   auto finish_stream = [&]() {
@@ -474,11 +540,9 @@ paged_decode_kernel(DecodeLaunch a) {
     }
     if (!complete) {
       if (slot == 0) {
-        split0 = cur;
-        has0 = true;
+        split0 = cur.start;
       } else {
-        split1 = cur;
-        has1 = true;
+        split1 = cur.start;
       }
     }
     __syncthreads();  // the combine buffer is free again
@@ -684,12 +748,22 @@ paged_decode_kernel(DecodeLaunch a) {
   while (cur.start < r1) finish_stream();
 
   // ---- Publish the split streams (uniform: every wave saw the same ones). ----
+  const bool has0 = split0 >= 0, has1 = split1 >= 0;
   if (has0 || has1) {
+    // The stream starting at flattened position p.
+    auto stream_from = [&](int p) {
+      const int s = uniform(seq_of(p));
+      const int pb = uniform(s_ps[s]);
+      const int nb = uniform(s_ps[s + 1]) - pb;
+      return stream_at(s, (p - Hh * pb) / nb);
+    };
+    const Stream st0 = stream_from(has0 ? split0 : split1);
+    const Stream st1 = stream_from(has1 ? split1 : split0);
     wait_vmem();  // the partials are complete at the coherence point before they are counted
     __syncthreads();
     if (tid < 2 && (tid == 0 ? has0 : has1)) {
-      const int st_start = tid == 0 ? split0.start : split1.start;
-      const int st_end = tid == 0 ? split0.end : split1.end;
+      const int st_start = tid == 0 ? st0.start : st1.start;
+      const int st_end = tid == 0 ? st0.end : st1.end;
       const int wa = range_owner(st_start, nwg, W);
       const int wb = range_owner(st_end - 1, nwg, W);
       const unsigned old = atomicAdd(a.counters + wa, 1u);
@@ -698,35 +772,41 @@ paged_decode_kernel(DecodeLaunch a) {
       s_last[tid] = last;
     }
     __syncthreads();
-    if (has0 && s_last[0]) merge_stream(split0);
-    if (has1 && s_last[1]) merge_stream(split1);
+    if (has0 && s_last[0]) merge_stream(st0);
+    if (has1 && s_last[1]) merge_stream(st1);
   }
 }
 
-template <int D, bool BF16, bool KV8>
+template <int D, bool BF16, bool KV8, bool APPEND>
 hipError_t launch_typed(const DecodeLaunch& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_kernel<D, BF16, KV8, kRing<D>>), dim3((unsigned)grid),
-                     dim3(64 * kWaves), 0, stream, a);
+  hipLaunchKernelGGL((paged_decode_kernel<D, BF16, KV8, APPEND, kRing<D, KV8, APPEND>>),
+                     dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool APPEND>
 hipError_t launch_dtype(const DecodeLaunch& a, int grid, bool bf16, hipStream_t stream) {
-  return bf16 ? launch_typed<D, true, KV8>(a, grid, stream)
-              : launch_typed<D, false, KV8>(a, grid, stream);
+  return bf16 ? launch_typed<D, true, KV8, APPEND>(a, grid, stream)
+              : launch_typed<D, false, KV8, APPEND>(a, grid, stream);
+}
+
+template <int D, bool APPEND>
+hipError_t launch_kv(const DecodeLaunch& a, int grid, bool bf16, bool kv_fp8, hipStream_t stream) {
+  return kv_fp8 ? launch_dtype<D, true, APPEND>(a, grid, bf16, stream)
+                : launch_dtype<D, false, APPEND>(a, grid, bf16, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeLaunch& a, int grid, int head_dim, bool bf16, bool kv_fp8,
-                         hipStream_t stream) {
+                         bool append, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
   if (head_dim == 128) {
-    return kv_fp8 ? launch_dtype<128, true>(a, grid, bf16, stream)
-                  : launch_dtype<128, false>(a, grid, bf16, stream);
+    return append ? launch_kv<128, true>(a, grid, bf16, kv_fp8, stream)
+                  : launch_kv<128, false>(a, grid, bf16, kv_fp8, stream);
   }
-  return kv_fp8 ? launch_dtype<64, true>(a, grid, bf16, stream)
-                : launch_dtype<64, false>(a, grid, bf16, stream);
+  return append ? launch_kv<64, true>(a, grid, bf16, kv_fp8, stream)
+                : launch_kv<64, false>(a, grid, bf16, kv_fp8, stream);
 }
 
 }  // namespace pkv

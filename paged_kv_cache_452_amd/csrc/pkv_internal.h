@@ -14,6 +14,41 @@ constexpr int kWaves = 4;           // wavefronts per decode workgroup
 constexpr int kMaxSeqs = 2048;      // sequences one decode launch plans for (LDS prefix sums)
 constexpr int kWorkgroupsPerCU = 2; // resident decode workgroups per compute unit
 
+// OCP E4M3 code of an fp32 value: round to nearest even, saturating at +-448, NaN kept (with its
+// sign), sign kept for zero. Integer arithmetic on the fp32 bits, so every device gives the same
+// code.
+__device__ __forceinline__ unsigned e4m3_code(float y) {
+  const unsigned bits = __float_as_uint(y);
+  const unsigned sign = (bits >> 24) & 0x80u;
+  const unsigned a = bits & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;  // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu; // |y| >= 448 (and infinity): saturate
+  const int e = (int)(a >> 23) - 127;        // exponent of |y| (fp32 denormals: -127)
+  if (e < -6) {
+    // Below the smallest normal 2^-6: code = |y| * 2^9 rounded, i.e. the 24-bit significand
+    // shifted right by 14 - e bits (a result of 8 is the smallest normal, code 0x08).
+    const int sh = 14 - e;
+    if (sh >= 32) return sign;
+    const unsigned sig = (a & 0x7FFFFFu) | 0x800000u;
+    unsigned q = sig >> sh;
+    const unsigned rem = sig & ((1u << sh) - 1u);
+    const unsigned half = 1u << (sh - 1);
+    q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+    return sign | q;
+  }
+  // Normal: 3 mantissa bits from 23, exponent field e + 7.
+  const unsigned m = a & 0x7FFFFFu;
+  unsigned q = m >> 20;
+  const unsigned rem = m & 0xFFFFFu;
+  q += (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
+  unsigned ef = (unsigned)(e + 7);
+  if (q == 8u) {
+    q = 0u;
+    ++ef;
+  }
+  return sign | (ef << 3) | q;
+}
+
 struct DecodeLaunch {
   void* out;
   const void* q;
@@ -34,11 +69,18 @@ struct DecodeLaunch {
   int max_blocks;       // block table row length
   int max_tokens;       // max_blocks * block_size: context lengths are clamped to it
   int sub_shift;        // log2(block_size / 16): sub-tiles per physical block = 1 << sub_shift
+  // Fused append (the step's new token of each sequence, at position context_len - 1, taken from
+  // these rows instead of the pool and written into the pool): [num_seqs][num_kv_heads][D].
+  const void* new_k;
+  const void* new_v;
+  float k_inv;          // fp8 pools: 1 / k_scale and 1 / v_scale (the new token's quantization)
+  float v_inv;
 };
 
-// Launch the decode kernel on `grid` workgroups. Returns a hipError_t.
+// Launch the decode kernel on `grid` workgroups (append: the fused variant that takes each
+// sequence's newest token from new_k / new_v). Returns a hipError_t.
 hipError_t launch_decode(const DecodeLaunch& a, int grid, int head_dim, bool bf16, bool kv_fp8,
-                         hipStream_t stream);
+                         bool append, hipStream_t stream);
 
 // reshape_and_cache into fp8 (E4M3) pools: code = e4m3(fl32(x * inv_scale)) per element.
 hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* k_pool,

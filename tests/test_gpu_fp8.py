@@ -223,3 +223,46 @@ def test_copy_blocks_fp8_pool_bit_exact():
     torch.cuda.synchronize()
     assert np.array_equal(codes(k), kb) and np.array_equal(codes(v), vb)
     pool.destroy()
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,lens,B,nwg", [
+    (32, 8, 128, [1, 2, 16, 17, 33, 700, 1500], 16, 0),
+    (12, 4, 64, [5, 64, 65, 300, 1], 32, 3),
+    (64, 2, 128, [40, 513], 16, 7),
+])
+def test_fused_append_decode_fp8_matches_oracle(Hq, Hkv, D, lens, B, nwg):
+    spec, t, b = _case8(Hq, Hkv, D, lens, seed=len(lens) + D + B, block_size=B)
+    ks, vs = 0.02, 0.015
+    k, v = b.k_pool[0], b.v_pool[0]
+    idx = []   # the NaN code into each new token's slot: overwritten before it is read, or it shows
+    for s, n in enumerate(lens):
+        blk = int(t.block_tables[s][(n - 1) // B])
+        for h in range(Hkv):
+            for d in range(D):
+                idx.append((oracle.pool_index8(False, blk, h, (n - 1) % B, d, Hkv, B, D),
+                            oracle.pool_index8(True, blk, h, (n - 1) % B, d, Hkv, B, D)))
+    ia = torch.tensor(idx, dtype=torch.long, device=DEV)
+    k.view(-1)[ia[:, 0]] = 0x7F
+    v.view(-1)[ia[:, 1]] = 0x7F
+    kb, vb = codes(k), codes(v)
+    oracle.reshape_and_cache8(kb, vb, b.new_key.cpu(), b.new_value.cpu(), oracle.BF16, ks, vs,
+                              t.slot_mapping, Hkv, D, B, t.num_blocks)
+    ref = oracle_decode8(b.q, kb, vb, t.block_tables, t.context_lens, spec.scale, ks, vs, Hq, Hkv,
+                         t.num_blocks, block_size=B)
+    maxc = int(max(lens))
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(len(lens), Hq, Hkv, D, B, maxc,
+                                                               nwg), DEV)
+    out = torch.empty_like(b.q)
+    say("fused append fp8", spec.name, nwg)
+    pkv.paged_attention_decode_append(out, b.q, b.new_key, b.new_value, k, v, b.block_tables,
+                                      b.context_lens, spec.scale, Hq, Hkv, D, B, maxc, nwg, ws,
+                                      kv_scales=(ks, vs))
+    torch.cuda.synchronize()
+    assert np.array_equal(codes(k), kb) and np.array_equal(codes(v), vb)
+    got = out.float().cpu().double().numpy()
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    # The new tokens' dequantized V rows reach |x| ~ 4, and a one-token sequence outputs one of
+    # them, rounded once to bf16 (up to 2^-8 |x|): hold max-abs to the bar relative to magnitude.
+    ref_mag = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(got - ref)))
+    assert rel <= 2e-3 and err <= 1e-2 * max(1.0, ref_mag / 2), (rel, err, ref_mag)

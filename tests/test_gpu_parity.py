@@ -264,3 +264,96 @@ def test_reshape_and_cache_skips_negative_and_past_pool_slots():
     pkv.reshape_and_cache(b.new_key, b.new_value, k, v, sm, t.num_blocks)
     torch.cuda.synchronize()
     assert np.array_equal(words(k), kw) and np.array_equal(words(v), vw)
+
+
+# ---- One fused step: paged_attention_decode_append = reshape_and_cache + decode ----
+
+def _poison_new_slots_(k, v, t, Hkv, D, B):
+    """NaN into the slot each sequence's new token goes to: the fused launch must write the token
+    there before it reads the slot's tile, or the NaN reaches the output."""
+    idx = []
+    for s, n in enumerate(t.context_lens):
+        n = int(n)
+        if n == 0:
+            continue
+        b = int(t.block_tables[s][(n - 1) // B])
+        for h in range(Hkv):
+            for d in range(D):
+                idx.append((oracle.pool_index(False, b, h, (n - 1) % B, d, Hkv, B, D),
+                            oracle.pool_index(True, b, h, (n - 1) % B, d, Hkv, B, D)))
+    ia = torch.tensor(idx, dtype=torch.long, device=k.device)
+    k.view(-1)[ia[:, 0]] = float("nan")
+    v.view(-1)[ia[:, 1]] = float("nan")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,lens,B,nwg", [
+    (8, 8, 128, torch.bfloat16, [1, 2, 15, 16, 17, 31, 32, 33], 16, 0),   # n = 1: only the new token
+    (32, 8, 128, torch.float16, [100, 257, 1000], 16, 0),
+    (12, 4, 64, torch.bfloat16, [5, 64, 65, 300], 16, 0),
+    (64, 2, 128, torch.bfloat16, [40, 513], 16, 3),                        # 2 head tiles, split
+    (4, 4, 64, torch.bfloat16, [0, 3, 0, 1, 16], 16, 0),                   # empty sequences
+    (32, 8, 128, torch.bfloat16, [3000, 7, 32 * 40 + 1, 17], 16, 200),     # many split streams
+    (32, 8, 128, torch.bfloat16, [1, 16, 17, 32, 33, 500, 4097], 32, 0),
+    (16, 1, 64, torch.float16, [2049, 2], 32, 5),
+])
+def test_fused_append_decode_matches_oracle(Hq, Hkv, D, dtype, lens, B, nwg):
+    spec, t, b = _random_case(Hq, Hkv, D, lens, dtype, seed=len(lens) * 3 + Hq + B, block_size=B)
+    k, v = _layer(b)
+    _poison_new_slots_(k, v, t, Hkv, D, B)
+    kw, vw = words(k), words(v)
+    oracle.reshape_and_cache(kw, vw, b.new_key.cpu(), b.new_value.cpu(), t.slot_mapping, Hkv, D, B,
+                             t.num_blocks)
+    ref = oracle_decode(b.q, None, None, t.block_tables, t.context_lens, spec.scale, Hq, Hkv,
+                        t.num_blocks, k_words=kw, v_words=vw, block_size=B)
+    maxc = max(int(max(lens)), 1)
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(len(lens), Hq, Hkv, D, B, maxc,
+                                                               nwg), DEV)
+    out = torch.empty_like(b.q)
+    say("fused append", spec.name, nwg)
+    pkv.paged_attention_decode_append(out, b.q, b.new_key, b.new_value, k, v, b.block_tables,
+                                      b.context_lens, spec.scale, Hq, Hkv, D, B, maxc, nwg, ws)
+    torch.cuda.synchronize()
+    assert_close(out, ref, spec.name)
+    assert np.array_equal(words(k), kw), "K pool differs from reshape_and_cache's"
+    assert np.array_equal(words(v), vw), "V pool differs from reshape_and_cache's"
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(out[s]).item() == 0
+        if n == 1:   # softmax over one token: the output is its value row, exactly
+            g = torch.arange(Hq, device=DEV) // (Hq // Hkv)
+            assert torch.equal(out[s].view(torch.int16), b.new_value[s][g].view(torch.int16))
+
+
+def test_fused_append_config4_80_layers_sampled():
+    """The benchmark's fused step on the 70B-shaped batch: every layer appends and decodes in one
+    launch; sampled outputs of sampled layers and the written slots against the oracle."""
+    spec = workloads.SPECS[4]
+    t = workloads.make_tables(spec)
+    say("fused config 4: allocating and filling 2 x 40 GiB")
+    batch = workloads.make_batch(spec, device=DEV, tables=t)
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    outs = torch.empty((spec.num_layers, S, Hq, D), dtype=batch.q.dtype, device=DEV)
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, 4096), DEV)
+    want = {}
+    for L in (0, 37, 79):
+        kw, vw = words(batch.k_pool[L]), words(batch.v_pool[L])
+        oracle.reshape_and_cache(kw, vw, batch.new_key.cpu(), batch.new_value.cpu(),
+                                 t.slot_mapping, Hkv, D, 16, t.num_blocks)
+        want[L] = (kw, vw)
+    say("fused config 4: 80 layers")
+    for L in range(spec.num_layers):
+        pkv.paged_attention_decode_append(outs[L], batch.q, batch.new_key, batch.new_value,
+                                          batch.k_pool[L], batch.v_pool[L], batch.block_tables,
+                                          batch.context_lens, spec.scale, Hq, Hkv, D, 16, 4096, 0,
+                                          ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(44)
+    for L, (kw, vw) in want.items():
+        assert np.array_equal(words(batch.k_pool[L]), kw) and np.array_equal(words(batch.v_pool[L]), vw)
+        pairs = [(int(s), int(h)) for s, h in zip(rng.integers(0, S, 48), rng.integers(0, Hq, 48))]
+        ref = oracle_decode(batch.q, None, None, t.block_tables, t.context_lens, spec.scale, Hq,
+                            Hkv, t.num_blocks, pairs=pairs, k_words=kw, v_words=vw)
+        got = torch.stack([outs[L, s, h] for s, h in pairs])
+        assert_close(got, ref, f"fused layer {L}")
+    del batch, outs
+    torch.cuda.empty_cache()
