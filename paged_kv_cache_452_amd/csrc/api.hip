@@ -84,6 +84,16 @@ bool device_visible(const int32_t* p, const int32_t** dev) {
   return true;
 }
 
+// Range weight of decode workgroups on odd-numbered XCDs (even ones weigh pkv::kEvenWeight): the
+// default below, or PKV_ODD_XCD_WEIGHT from the environment (read at every call), clamped to
+// [kEvenWeight / 2, kEvenWeight].
+constexpr int kDefaultOddXcdWeight = 900;
+int odd_xcd_weight() {
+  int v = kDefaultOddXcdWeight;
+  if (const char* e = getenv("PKV_ODD_XCD_WEIGHT")) v = atoi(e);
+  return v < pkv::kEvenWeight / 2 ? pkv::kEvenWeight / 2 : v > pkv::kEvenWeight ? pkv::kEvenWeight : v;
+}
+
 // Bytes of one block's region in one layer of one of the two pools.
 size_t block_bytes_of(const pkv_pool* p) {
   return (size_t)p->num_kv_heads * p->block_size * p->head_dim * elem_bytes(p->dtype);
@@ -409,6 +419,7 @@ pkv_status decode_impl(void* out, const void* q, const void* new_k, const void* 
   a.sub_shift = block_size == 32 ? 1 : 0;
   a.new_k = new_k;
   a.new_v = new_v;
+  a.odd_weight = odd_xcd_weight();
   const float one = 1.0f;
   a.k_inv = one / k_scale;
   a.v_inv = one / v_scale;

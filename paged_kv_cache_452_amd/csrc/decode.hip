@@ -158,14 +158,6 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // the exact, deep waits of the common path.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Workgroup ranges: workgroup w of nwg covers flattened positions [start(w), start(w + 1)).
-__device__ __forceinline__ int range_start(int w, int nwg, int W) {
-  return (int)((long)w * W / nwg);
-}
-// The workgroup whose range holds position p (0 <= p < W): the last w with start(w) <= p.
-__device__ __forceinline__ int range_owner(int p, int nwg, int W) {
-  return (int)(((long)(p + 1) * nwg - 1) / W);
-}
 
 template <int D, bool BF16, bool KV8, bool APPEND, int RING>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void
@@ -243,8 +235,23 @@ paged_decode_kernel(DecodeLaunch a) {
   const int nwg = min((int)gridDim.x, W);
   const int wg = blockIdx.x;
   if (wg >= nwg) return;  // uniform over the workgroup
-  const int r0 = range_start(wg, nwg, W);
-  const int r1 = range_start(wg + 1, nwg, W);
+  // Weighted ranges only when they can help and cannot hurt:
+  //  * every range keeps at least one position (W >= 2 nwg with weights in [kEvenWeight / 2,
+  //    kEvenWeight]): the split-stream bookkeeping needs non-empty ranges;
+  //  * the equal split does not already fall on stream boundaries (all streams of one length L
+  //    with W / nwg a whole number of streams): then it splits no stream, and any weighting
+  //    would add a merge to every workgroup. Every workgroup sees the same plan, so all decide
+  //    alike.
+  bool aligned = W % nwg == 0;
+  if (aligned) {
+    const int L = s_ps[1] - s_ps[0];  // units of the first sequence
+    aligned = L > 0 && (W / nwg) % L == 0;
+    for (int i = tid; aligned && i < S; i += kThreads) aligned = s_ps[i + 1] - s_ps[i] == L;
+    aligned = __syncthreads_and(aligned);
+  }
+  const int odd_w = W >= 2 * nwg && !aligned ? a.odd_weight : kEvenWeight;
+  const int r0 = range_start(wg, nwg, W, odd_w);
+  const int r1 = range_start(wg + 1, nwg, W, odd_w);
 
   // Sequence whose streams hold flattened position p: the last s with Hh * s_ps[s] <= p.
   auto seq_of = [&](int p) {
@@ -556,9 +563,9 @@ paged_decode_kernel(DecodeLaunch a) {
   // XCDs.
   auto merge_stream = [&](const Stream& st) {
     if (head >= st.nvalid) return;  // uniform over each 16-lane head group
-    const int wa = range_owner(st.start, nwg, W);
-    const int np = range_owner(st.end - 1, nwg, W) - wa + 1;
-    const int slot_a = range_start(wa, nwg, W) == st.start ? 0 : 1;
+    const int wa = range_owner(st.start, nwg, W, odd_w);
+    const int np = range_owner(st.end - 1, nwg, W, odd_w) - wa + 1;
+    const int slot_a = range_start(wa, nwg, W, odd_w) == st.start ? 0 : 1;
     auto part_idx = [&](int k) {  // partial index of part k (workgroup wa + k)
       return ((size_t)(wa + k) * 2 + (k == 0 ? slot_a : 0)) * kMaxGroupTile + head;
     };
@@ -764,8 +771,8 @@ paged_decode_kernel(DecodeLaunch a) {
     if (tid < 2 && (tid == 0 ? has0 : has1)) {
       const int st_start = tid == 0 ? st0.start : st1.start;
       const int st_end = tid == 0 ? st0.end : st1.end;
-      const int wa = range_owner(st_start, nwg, W);
-      const int wb = range_owner(st_end - 1, nwg, W);
+      const int wa = range_owner(st_start, nwg, W, odd_w);
+      const int wb = range_owner(st_end - 1, nwg, W, odd_w);
       const unsigned old = atomicAdd(a.counters + wa, 1u);
       const int last = old == (unsigned)(wb - wa);
       if (last) __hip_atomic_store(a.counters + wa, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -49,6 +49,40 @@ __device__ __forceinline__ unsigned e4m3_code(float y) {
   return sign | (ef << 3) | q;
 }
 
+// ---- Decode workgroup ranges ----
+// Workgroups are dispatched round-robin over the 8 XCDs (XCD = blockIdx % 8), and on MI355X the
+// odd-numbered XCDs stream measurably slower (about 9% on the 70B-shaped decode, on every board
+// measured). Each workgroup's share of the flattened positions is therefore proportional to a
+// weight: kEvenWeight on even XCDs, odd_weight on odd ones, so that all finish together.
+// Workgroup w covers [range_start(w), range_start(w + 1)).
+constexpr int kEvenWeight = 1024;
+
+// C(w): sum of the weights of workgroups 0 .. w - 1.
+__host__ __device__ inline long long range_cum_weight(int w, int odd_weight) {
+  const int r = w & 7;
+  return (long long)(w >> 3) * (4LL * kEvenWeight + 4LL * odd_weight) +
+         (long long)((r + 1) / 2) * kEvenWeight + (long long)(r / 2) * odd_weight;
+}
+
+__host__ __device__ inline int range_start(int w, int nwg, int W, int odd_weight) {
+  return (int)((long long)W * range_cum_weight(w, odd_weight) /
+               range_cum_weight(nwg, odd_weight));
+}
+
+// The workgroup whose range holds position p (0 <= p < W): the last w < nwg with
+// range_start(w) <= p, i.e. with C(w) <= ceil((p + 1) C(nwg) / W) - 1.
+__host__ __device__ inline int range_owner(int p, int nwg, int W, int odd_weight) {
+  const long long x = ((long long)(p + 1) * range_cum_weight(nwg, odd_weight) - 1) / W;
+  const long long period = 4LL * kEvenWeight + 4LL * odd_weight;
+  const long long q = x / period;
+  const long long rem = x - q * period;
+  int r = 7;
+  while (r > 0 && (long long)((r + 1) / 2) * kEvenWeight + (long long)(r / 2) * odd_weight > rem)
+    --r;
+  const long long w = q * 8 + r;
+  return (int)(w < nwg - 1 ? w : nwg - 1);
+}
+
 struct DecodeLaunch {
   void* out;
   const void* q;
@@ -75,6 +109,7 @@ struct DecodeLaunch {
   const void* new_v;
   float k_inv;          // fp8 pools: 1 / k_scale and 1 / v_scale (the new token's quantization)
   float v_inv;
+  int odd_weight;       // range weight of workgroups on odd XCDs (even ones: kEvenWeight)
 };
 
 // Launch the decode kernel on `grid` workgroups (append: the fused variant that takes each
