@@ -245,3 +245,25 @@ def test_swap_blocks_argument_errors():
     assert f(dev._h, host._h, FAKE + 2, FAKE, 1, 0, None) == ALIGN
     for p in (dev, host, other, fp8):
         p.destroy()
+
+
+def test_fused_append_argument_errors():
+    lib = pkv.load_library()
+    f = lib.paged_attention_decode_append
+    f8 = lib.paged_attention_decode_append_fp8
+
+    def call(key=FAKE, value=FAKE, s=4, d=128, nwg=1, ws=None, wsb=0, kv=FAKE):
+        return f(FAKE, FAKE, key, value, kv, FAKE, FAKE, FAKE, 0.1, 32, 8, d, 16, s, 8, 128, nwg,
+                 0, ws, wsb, None)
+
+    assert call(key=None) == INVALID                        # the new rows are required
+    assert call(value=None) == INVALID
+    assert call(key=FAKE + 4) == ALIGN
+    assert call(d=96) == UNSUPPORTED
+    assert call(s=0, key=None, value=None) == OK              # nothing to do
+    assert call(nwg=32) == WORKSPACE
+    assert call(kv=FAKE + 8) == ALIGN
+    assert f8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 0.0, 1.0, 32, 8, 128, 16, 4, 8,
+              128, 1, 0, None, 0, None) == INVALID            # k_scale must be > 0
+    assert f8(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 1.0, 1.0, 32, 8, 128, 16, 4, 8,
+              128, 1, 0, None, 0, None) == INVALID
