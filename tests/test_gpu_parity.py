@@ -357,3 +357,32 @@ def test_fused_append_config4_80_layers_sampled():
         assert_close(got, ref, f"fused layer {L}")
     del batch, outs
     torch.cuda.empty_cache()
+
+
+def test_max_sequences_per_launch():
+    """2048 sequences (the most one launch plans for), ragged short contexts, some empty."""
+    rng = np.random.default_rng(2048)
+    lens = rng.integers(0, 70, size=2048).astype(np.int32)
+    lens[::97] = 0
+    spec, t, b = _random_case(8, 2, 64, lens, seed=77, extra_blocks=3)
+    k, v = _layer(b)
+    say("2048 sequences")
+    out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 8, 2, int(lens.max()))
+    torch.cuda.synchronize()
+    ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 8, 2, t.num_blocks)
+    assert_close(out, ref, "2048 sequences")
+    assert torch.count_nonzero(out[lens == 0]).item() == 0
+
+
+@pytest.mark.parametrize("nwg", [0, 5])
+def test_wide_group_many_head_tiles(nwg):
+    """128 query heads on one kv head: 8 head tiles per (sequence, kv head), each its own stream
+    over the same tiles."""
+    spec, t, b = _random_case(128, 1, 128, [300, 17, 1024], seed=128)
+    k, v = _layer(b)
+    say("128/1 heads", nwg)
+    out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 128, 1, 1024, nwg)
+    torch.cuda.synchronize()
+    ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 128, 1,
+                        t.num_blocks)
+    assert_close(out, ref, spec.name)
