@@ -3,11 +3,13 @@
 // Work decomposition. Every (sequence s, kv head g, tile of <= 16 query heads) is one *stream* of
 // nb_s = ceil(n_s / 16) blocks. The streams are laid end to end, sequence-major, into one
 // flattened space of W = sum_s nb_s * (kv heads * head tiles) block positions, and the launch's
-// workgroups cut that space into equal contiguous ranges. A workgroup therefore reads the same
-// number of blocks (to within one) whatever the mix of context lengths: a 32k-token sequence is
-// spread over many workgroups and a batch of short ones is packed into few, with no per-sequence
-// partition size to tune and no tail of idle compute units. Each workgroup derives the plan itself
-// from context_lens (a prefix sum in LDS), so the host needs no device data.
+// workgroups cut that space into contiguous ranges: equal ones, or (when the equal cut would split
+// streams anyway) ranges weighted by the XCD a workgroup runs on, since odd-numbered XCDs stream
+// measurably slower (see range_start). A workgroup's share is thus fixed whatever the mix of
+// context lengths: a 32k-token sequence is spread over many workgroups and a batch of short ones
+// is packed into few, with no per-sequence partition size to tune and no tail of idle compute
+// units. Each workgroup derives the plan itself from context_lens (a prefix sum in LDS), so the
+// host needs no device data.
 //
 // Inside a range the four wavefronts interleave block by block (wave i takes positions
 // r0 + i, r0 + i + 4, ...), so all four always work on the same stream. Per 16-token block a
@@ -33,6 +35,12 @@
 // boundary leaves an fp32 partial (m, l, O) in the workspace; the last of its workgroups to finish
 // (an agent-scope counter, reset by that workgroup) merges all of them in range order, so the
 // result does not depend on which workgroup came last.
+//
+// Variants (template parameters): head dim 64 or 128; bf16 or fp16 q/out; 16-bit pools or fp8
+// (E4M3) pools whose codes are widened to the q type in registers, with the pool scales folded
+// into the score scale and the output normalisation; and APPEND, the fused step, in which every
+// workgroup first writes the new token of each stream whose last unit it owns into the pool
+// (before it reads any tile), so that the main loop is the same in every variant.
 //
 // Softmax identity used by both combines: with per-part reference m_p, l_p = sum exp(x - m_p)
 // and O_p = sum exp(x - m_p) v, the full result is
