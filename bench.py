@@ -42,21 +42,32 @@ def algorithmic_bytes(lens, num_q_heads, num_kv_heads, head_dim, elem=2, block=1
     return kv + qo + tables + 4 * len(lens)
 
 
+def code_hash(text: str) -> str:
+    """Hash of a C++ source with its // comments, trailing spaces and blank lines removed, so that
+    a comment edit does not invalidate counters taken on the same code."""
+    lines = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def source_hash() -> str:
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(DECODE_SRC, encoding="utf-8") as f:
+        return code_hash(f.read())
 
 
 def measured_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source and this workload."""
+    on the current kernel code (comments aside) and this workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             recs = json.load(f).get("records", [])
     except (OSError, ValueError, AttributeError):
         return None
     for rec in recs:
-        if rec.get("decode_source_sha256_16") == source_hash() and rec.get("workload") == workload:
+        if rec.get("decode_code_sha256_16") == source_hash() and rec.get("workload") == workload:
             return rec.get("bytes_per_launch")
     return None
 
