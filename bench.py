@@ -21,7 +21,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth, GB/s
 METRIC = "decode KV-read GB/s (% of MI355X HBM peak) + tokens/s per layer-step"
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_452_amd", "csrc", "decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_452_amd", "csrc", f)
+               for f in ("decode.hip", "pkv_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
@@ -54,8 +55,12 @@ def code_hash(text: str) -> str:
 
 
 def source_hash() -> str:
-    with open(DECODE_SRC, encoding="utf-8") as f:
-        return code_hash(f.read())
+    """Code hash of the decode kernel's sources (the kernel file and the internal header)."""
+    text = ""
+    for path in DECODE_SRCS:
+        with open(path, encoding="utf-8") as f:
+            text += f.read() + "\n"
+    return code_hash(text)
 
 
 def measured_traffic(workload: str):
