@@ -175,11 +175,13 @@ pkv_status reshape_and_cache_fp8(const void* key, const void* value, void* k_poo
                                  float k_scale, float v_scale, hipStream_t stream);
 
 /*
- * Workgroups paged_attention_decode launches when it is passed num_workgroups == 0: enough to fill
- * every compute unit of the current device, fewer for small batches. The decode lays every
- * (sequence, kv head) stream of blocks end to end and gives each workgroup an equal contiguous
- * share, so long and skewed sequences are spread evenly; a stream cut between workgroups is
- * joined by a log-sum-exp merge of fp32 partial results. Returns 0 on invalid arguments.
+ * Workgroups paged_attention_decode launches when it is passed num_workgroups == 0: one per 64
+ * block positions (sequences x kv heads x head tiles x blocks of max_context_len), but at least
+ * one per stream, and at most two per compute unit of the current device. The decode lays every
+ * (sequence, kv head) stream of blocks end to end and gives each workgroup a contiguous share
+ * (equal, or weighted by the XCD it runs on), so long and skewed sequences are spread evenly; a
+ * stream cut between workgroups is joined by a log-sum-exp merge of fp32 partial results.
+ * Returns 0 on invalid arguments.
  */
 int paged_attention_num_workgroups(int num_seqs, int num_q_heads, int num_kv_heads,
                                    int max_context_len, int block_size);
@@ -221,7 +223,8 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  *                Calls that may run concurrently need separate workspaces.
  * At most 2048 sequences per call (PKV_ERR_UNSUPPORTED above).
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_ALIGNMENT, PKV_ERR_WORKSPACE,
- * PKV_ERR_HIP. Deterministic: identical inputs give bit-identical outputs (no atomics).
+ * PKV_ERR_HIP. Deterministic: identical inputs give bit-identical outputs (split streams are
+ * merged in a fixed order, whichever workgroup finishes last).
  */
 pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_tables, const int32_t* context_lens,

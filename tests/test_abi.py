@@ -133,12 +133,14 @@ def test_workspace_and_workgroup_choice():
                              (66, 32, 8, 32768), (4, 4, 4, 41), (1, 8, 1, 1 << 20)]:
         g = pkv.paged_attention_num_workgroups(S, Hq, Hkv, maxc, 16)
         heads_tiles = -(-(Hq // Hkv) // 16)
-        positions = S * Hkv * heads_tiles * -(-maxc // 16)
-        assert 1 <= g <= max(1, -(-positions // 64))
+        streams = S * Hkv * heads_tiles
+        positions = streams * -(-maxc // 16)
+        assert 1 <= g <= max(1, -(-positions // 64), streams)
+        assert g >= min(streams, 2 * 256)   # at least one per stream (up to the resident limit)
         assert g <= 2 * 304   # two resident workgroups per compute unit
         assert pkv.paged_attention_workspace_bytes(S, Hq, Hkv, 128, 16, maxc, 0) == _ws(g)
-    # tiny batch: 4 sequences x 3 blocks x 4 kv heads = 48 positions -> 1 workgroup
-    assert pkv.paged_attention_num_workgroups(4, 4, 4, 41, 16) == 1
+    # tiny batch: 4 sequences x 4 kv heads = 16 streams of <= 3 blocks -> one workgroup each
+    assert pkv.paged_attention_num_workgroups(4, 4, 4, 41, 16) == 16
     assert pkv.paged_attention_num_workgroups(4, 30, 8, 41, 16) == 0
 
 
