@@ -481,6 +481,39 @@ paged_decode_kernel(DecodeLaunch a) {
     }
   };
 
+  // The four waves' (m, l, O) of the stream just combined in LDS, folded for head `head`, dims
+  // d0 .. d0 + kDims (the caller checks head < nvalid).
+  auto combine_waves = [&](float& M, float& L, float* acc) {
+    M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][head]);
+    L = 0.f;
+#pragma unroll
+    for (int i = 0; i < kDims; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw_ = sm_m[w][head];
+      const float c = mw_ == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw_ - M);  // idle wave
+      L += c * sm_l[w][head];
+#pragma unroll
+      for (int i = 0; i < kDims; ++i) acc[i] += c * sm_o[w][head][d0 + i];
+    }
+  };
+  // A split stream's partial in partial slot `slot` of this workgroup, written through to the
+  // device's coherence point (agent-scope stores): the merging workgroup may run on another XCD,
+  // behind another L2.
+  auto store_partial = [&](int slot, float M, float L, const float* acc) {
+    const size_t pidx = ((size_t)wg * 2 + slot) * kMaxGroupTile + head;
+    float* po = a.ws_o + pidx * D + d0;
+#pragma unroll
+    for (int i = 0; i < kDims; ++i)
+      __hip_atomic_store(po + i, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane % kLanesPerHead == 0) {
+      __hip_atomic_store(a.ws_ml + pidx * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ws_ml + pidx * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
   // Split streams of this range: 0 = the one holding r0, 1 = the one holding r1 - 1.
   // Only their start positions stay live through the main loop (scalar registers are the scarce
   // resource there); the merge rebuilds the streams from them. -1: no such stream.
@@ -520,37 +553,16 @@ paged_decode_kernel(DecodeLaunch a) {
 
     const bool complete = cur.start >= r0 && cur.end <= r1;  // uniform
     const int slot = cur.start <= r0 ? 0 : 1;
-    if (head < cur.nvalid) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][head]);
-      float L = 0.f;
-      float acc[kDims];
-#pragma unroll
-      for (int i = 0; i < kDims; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw_ = sm_m[w][head];
-        const float c = mw_ == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw_ - M);  // idle wave
-        L += c * sm_l[w][head];
-#pragma unroll
-        for (int i = 0; i < kDims; ++i) acc[i] += c * sm_o[w][head][d0 + i];
-      }
+    // The stream holding r1 - 1 (slot 1) is always the last one this range finishes, after the
+    // main loop: its waves' results stay in LDS for the publish step, which may merge the stream
+    // straight from there.
+    if (head < cur.nvalid && (complete || slot == 0)) {
+      float M, L, acc[kDims];
+      combine_waves(M, L, acc);
       if (complete) {
         store_out((size_t)cur.s * a.num_q_heads + cur.h0 + head, acc, L);
       } else {
-        // Written through to the device's coherence point (agent-scope stores): the merging
-        // workgroup may run on another XCD, behind another L2.
-        const size_t pidx = ((size_t)wg * 2 + slot) * kMaxGroupTile + head;
-        float* po = a.ws_o + pidx * D + d0;
-#pragma unroll
-        for (int i = 0; i < kDims; ++i)
-          __hip_atomic_store(po + i, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (lane % kLanesPerHead == 0) {
-          __hip_atomic_store(a.ws_ml + pidx * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(a.ws_ml + pidx * 2 + 1, L, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        }
+        store_partial(0, M, L, acc);
       }
     }
     if (!complete) {
@@ -560,7 +572,7 @@ paged_decode_kernel(DecodeLaunch a) {
         split1 = cur.start;
       }
     }
-    __syncthreads();  // the combine buffer is free again
+    if (complete || slot == 0) __syncthreads();  // the combine buffer is free again
     cur = nxt;
   };
 
@@ -569,7 +581,9 @@ paged_decode_kernel(DecodeLaunch a) {
   // of the round before using any of them (one memory round trip per round), then folds the round
   // into a running maximum. Loads are agent-scope: the partials were written through from other
   // XCDs.
-  auto merge_stream = [&](const Stream& st) {
+  // own: part 0 is this workgroup's, passed in as (own_m, own_l, own_acc) instead of stored.
+  auto merge_stream = [&](const Stream& st, bool own, float own_m, float own_l,
+                          const float* own_acc) {
     if (head >= st.nvalid) return;  // uniform over each 16-lane head group
     const int wa = range_owner(st.start, nwg, W, odd_w);
     const int np = range_owner(st.end - 1, nwg, W, odd_w) - wa + 1;
@@ -596,6 +610,14 @@ paged_decode_kernel(DecodeLaunch a) {
 #pragma unroll
         for (int i = 0; i < kDims / 2; ++i)
           ov[u][i] = __hip_atomic_load(po + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (own && k0 == 0) {  // the same fp32 values the partial would have held
+        mp[0] = own_m;
+        lp[0] = own_l;
+#pragma unroll
+        for (int i = 0; i < kDims / 2; ++i)
+          ov[0][i] = (unsigned long long)__float_as_uint(own_acc[2 * i]) |
+                     (unsigned long long)__float_as_uint(own_acc[2 * i + 1]) << 32;
       }
       float Mr = M;
 #pragma unroll
@@ -763,6 +785,8 @@ paged_decode_kernel(DecodeLaunch a) {
   while (cur.start < r1) finish_stream();
 
   // ---- Publish the split streams (uniform: every wave saw the same ones). ----
+  // A split stream's parts are counted on the arrival counter of its first part's workgroup; the
+  // part that brings the count to the number of parts merges them all and resets the counter.
   const bool has0 = split0 >= 0, has1 = split1 >= 0;
   if (has0 || has1) {
     // The stream starting at flattened position p.
@@ -774,21 +798,53 @@ paged_decode_kernel(DecodeLaunch a) {
     };
     const Stream st0 = stream_from(has0 ? split0 : split1);
     const Stream st1 = stream_from(has1 ? split1 : split0);
-    wait_vmem();  // the partials are complete at the coherence point before they are counted
+    const int wa0 = range_owner(st0.start, nwg, W, odd_w);
+    const int np0 = range_owner(st0.end - 1, nwg, W, odd_w) - wa0 + 1;
+    const int np1 = range_owner(st1.end - 1, nwg, W, odd_w) - wg + 1;  // st1 starts in this range
+    // Split 1's own part, folded once from the combine buffer: both ways of finishing it below
+    // use these very values, so the result cannot depend on which workgroup arrives last.
+    float m1 = 0.f, l1 = 0.f, acc1[kDims];
+#pragma unroll
+    for (int i = 0; i < kDims; ++i) acc1[i] = 0.f;
+    if (has1 && head < st1.nvalid) combine_waves(m1, l1, acc1);
+    wait_vmem();  // split 0's partial is complete at the coherence point before it is counted
     __syncthreads();
-    if (tid < 2 && (tid == 0 ? has0 : has1)) {
-      const int st_start = tid == 0 ? st0.start : st1.start;
-      const int st_end = tid == 0 ? st0.end : st1.end;
-      const int wa = range_owner(st_start, nwg, W, odd_w);
-      const int wb = range_owner(st_end - 1, nwg, W, odd_w);
-      const unsigned old = atomicAdd(a.counters + wa, 1u);
-      const int last = old == (unsigned)(wb - wa);
-      if (last) __hip_atomic_store(a.counters + wa, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last[tid] = last;
+    if (tid == 0 && has0) {
+      const unsigned old = atomicAdd(a.counters + wa0, 1u);
+      const int last = old == (unsigned)(np0 - 1);
+      if (last) __hip_atomic_store(a.counters + wa0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last[0] = last;
+    }
+    if (tid == 1 && has1) {
+      // Split 1 begins here, so its counter is this workgroup's. When every other part has
+      // already arrived, this workgroup is the last: it merges at once, taking its own part from
+      // the combine buffer, and skips storing, draining and counting that part.
+      const unsigned seen =
+          __hip_atomic_load(a.counters + wg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int fast = seen == (unsigned)(np1 - 1);
+      if (fast) __hip_atomic_store(a.counters + wg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last[1] = fast;
     }
     __syncthreads();
-    if (has0 && s_last[0]) merge_stream(st0);
-    if (has1 && s_last[1]) merge_stream(st1);
+    if (has0 && s_last[0]) merge_stream(st0, false, 0.f, 0.f, acc1);
+    if (has1) {
+      if (s_last[1]) {
+        merge_stream(st1, true, m1, l1, acc1);
+      } else {
+        if (head < st1.nvalid) store_partial(1, m1, l1, acc1);
+        wait_vmem();
+        __syncthreads();
+        if (tid == 1) {
+          const unsigned old = atomicAdd(a.counters + wg, 1u);
+          const int last = old == (unsigned)(np1 - 1);
+          if (last)
+            __hip_atomic_store(a.counters + wg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_last[1] = last;
+        }
+        __syncthreads();
+        if (s_last[1]) merge_stream(st1, false, 0.f, 0.f, acc1);
+      }
+    }
   }
 }
 

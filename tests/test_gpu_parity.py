@@ -386,3 +386,26 @@ def test_wide_group_many_head_tiles(nwg):
     ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 128, 1,
                         t.num_blocks)
     assert_close(out, ref, spec.name)
+
+
+@pytest.mark.parametrize("num_workgroups", [0, 37, 300])
+def test_split_streams_are_deterministic(num_workgroups):
+    """Split streams are merged by whichever of their workgroups arrives last (directly from its
+    combine buffer when all others are in, else after storing its own part): repeated launches,
+    whose arrival orders differ, must give bit-identical outputs, and the oracle's values."""
+    spec, t, b = _random_case(32, 8, 128, [4000, 17, 900, 2500, 1, 333], seed=91)
+    k, v = _layer(b)
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(6, 32, 8, 128, 16, 4000,
+                                                               num_workgroups), DEV)
+    say("determinism", num_workgroups)
+    first = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, 4000,
+                       num_workgroups, workspace=ws).clone()
+    torch.cuda.synchronize()
+    ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 32, 8,
+                        t.num_blocks)
+    assert_close(first, ref, f"{num_workgroups} workgroups")
+    for rep in range(12):
+        out = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, 4000,
+                         num_workgroups, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), first.view(torch.int16)), f"rep {rep}"
