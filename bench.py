@@ -148,11 +148,9 @@ def bench_copy_blocks(args) -> int:
 
     spec = workloads.SPECS[4]
     L, NB, Hkv, D = spec.num_layers, 16384, spec.num_kv_heads, spec.head_dim
-    k = torch.empty((L, NB, Hkv, 16 * D), dtype=torch.bfloat16, device="cuda")
-    v = torch.empty_like(k)
-    k.view(torch.int16).random_(-32768, 32767)
-    v.view(torch.int16).random_(-32768, 32767)
-    pool = pkv.kv_pool_create(k, v, k.numel() * 2, L, NB, Hkv, D, 16, pkv.PKV_BF16)
+    kv = workloads.new_pool(L, NB, Hkv, 16, D, torch.bfloat16, "cuda")
+    kv.view(torch.int16).random_(-32768, 32767)
+    pool = pkv.kv_pool_create(kv, kv.numel() * 2, L, NB, Hkv, D, 16, pkv.PKV_BF16)
     rng = np.random.default_rng(7)
     perm = rng.permutation(NB).astype(np.int32)
     npairs = 64
@@ -173,14 +171,12 @@ def bench_copy_blocks(args) -> int:
     moved = 2 * npairs * L * 2 * block_bytes
     gbs = moved / (us * 1e-6) / 1e9
     # CPU oracle beside it: the same copies as numpy block assignments on host copies of 8 layers.
-    kh = k[:8].view(torch.int16).cpu().numpy()
-    vh = v[:8].view(torch.int16).cpu().numpy()
+    kvh = kv[:8].view(torch.int16).cpu().numpy()
     s_np, d_np = perm[:npairs], perm[npairs:2 * npairs]
     t0 = time.perf_counter()
     reps = 0
     while time.perf_counter() - t0 < 2.0:
-        kh[:, d_np] = kh[:, s_np]
-        vh[:, d_np] = vh[:, s_np]
+        kvh[:, d_np] = kvh[:, s_np]
         reps += 1
     cpu_s = (time.perf_counter() - t0) / reps
     cpu_gbs = 2 * npairs * 8 * 2 * block_bytes / cpu_s / 1e9
@@ -190,7 +186,7 @@ def bench_copy_blocks(args) -> int:
         "us_per_call": round(us, 2), "higher_is_better": True, "data": "synthetic",
         "dtype": "bf16",
         "config": {"workload": "copy-on-write burst on the 70B-shaped pool: 64 block copies x "
-                               "80 layers x (K, V), 32 KiB per block region",
+                               "80 layers, K and V (64 KiB per block region)",
                    "bytes_per_call": moved},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
@@ -215,14 +211,12 @@ def bench_swap(args) -> int:
     spec = workloads.SPECS[4]
     t = workloads.make_tables(spec)
     L, NB, Hkv, D, B = spec.num_layers, t.num_blocks, spec.num_kv_heads, spec.head_dim, 16
-    k = torch.empty((L, NB, Hkv, B * D), dtype=torch.bfloat16, device="cuda")
-    v = torch.empty_like(k)
+    kv = workloads.new_pool(L, NB, Hkv, B, D, torch.bfloat16, "cuda")
     victims = np.concatenate([t.block_tables[0], t.block_tables[1]]).astype(np.int32)
     n = victims.shape[0]
-    hk = torch.empty((L, n, Hkv, B * D), dtype=torch.bfloat16, pin_memory=True)
-    hv = torch.empty_like(hk, pin_memory=True)
-    dpool = pkv.kv_pool_create(k, v, k.numel() * 2, L, NB, Hkv, D, B, pkv.PKV_BF16)
-    hpool = pkv.kv_pool_create(hk, hv, hk.numel() * 2, L, n, Hkv, D, B, pkv.PKV_BF16)
+    hkv = workloads.new_pool(L, n, Hkv, B, D, torch.bfloat16, "cpu", pin_memory=True)
+    dpool = pkv.kv_pool_create(kv, kv.numel() * 2, L, NB, Hkv, D, B, pkv.PKV_BF16)
+    hpool = pkv.kv_pool_create(hkv, hkv.numel() * 2, L, n, Hkv, D, B, pkv.PKV_BF16)
     dev_ids = torch.from_numpy(victims).cuda()
     host_ids = torch.arange(n, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -259,21 +253,21 @@ def bench_swap(args) -> int:
     rt = 2 * moved / ((ms_out + ms_in) * 1e-3) / 1e9
     # CPU oracle beside it: the same block gather as numpy on host copies of 2 layers.
     rng = np.random.default_rng(3)
-    kh = rng.integers(0, 65535, size=(2, NB, Hkv * B * D), dtype=np.uint16)
-    dst = np.zeros((2, n, Hkv * B * D), np.uint16)
+    kh = rng.integers(0, 65535, size=(2, NB, 2 * Hkv * B * D), dtype=np.uint16)
+    dst = np.zeros((2, n, 2 * Hkv * B * D), np.uint16)
     t0 = time.perf_counter()
     creps = 0
     while time.perf_counter() - t0 < 2.0:
         dst[:] = kh[:, victims]
         creps += 1
-    cpu_gbs = 2 * n * Hkv * B * D * 2 / ((time.perf_counter() - t0) / creps) / 1e9
+    cpu_gbs = 2 * n * 2 * Hkv * B * D * 2 / ((time.perf_counter() - t0) / creps) / 1e9
     print(json.dumps({
         "metric": "swap_blocks GB/s over the host link (swap out + swap in)", "value": round(rt, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
         "higher_is_better": True, "data": "synthetic", "dtype": "bf16",
         "config": {"workload": "preempt 2 of 64 sequences of the 70B-shaped batch: 512 blocks x 80 "
-                               "layers x (K, V), 32 KiB per block region, to a pinned host pool "
-                               "and back", "bytes_per_call": moved},
+                               "layers, K and V (64 KiB per block region), to a pinned host "
+                               "pool and back", "bytes_per_call": moved},
         "swap_out_ms": round(ms_out, 3), "swap_out_gbs": round(out_gbs, 2),
         "swap_in_ms": round(ms_in, 3), "swap_in_gbs": round(in_gbs, 2),
         "dma_copy_same_bytes": {"d2h_gbs": round(gbs(ms_d2h), 2), "h2d_gbs": round(gbs(ms_h2d), 2),
@@ -281,8 +275,8 @@ def bench_swap(args) -> int:
         "roofline": {"bound": "host link", "achieved": round(rt, 2), "peak": PCIE_PEAK_GBS,
                      "unit": "GB/s", "frac": round(rt / PCIE_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                         "sample": "numpy gather of the same 512 blocks from host copies of 2 "
-                                   "layers of one pool"},
+                         "sample": "numpy gather of the same 512 blocks (K and V) from host "
+                                   "copies of 2 layers of one pool"},
     }), flush=True)
     for p in (dpool, hpool):
         p.destroy()

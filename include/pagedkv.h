@@ -40,13 +40,20 @@
  * ---------------------------------------------------------------------------------------------
  * KV pool layout (the one data format this ABI defines)
  *
- * K and V are two separate pools of 16-bit elements. Element (layer L, block b, kv head h,
- * token slot t in [0,B), dim d in [0,D)) lives at element index
+ * One pool holds K and V of every layer: [layer][block][kv_head][K tile, V tile], one tile = B*D
+ * elements (4 KiB for D=128, B=16 in 16-bit). Key element (layer L, block b, kv head h, token
+ * slot t in [0,B), dim d in [0,D)) lives at element index
  *
- *     ((L * num_blocks + b) * num_kv_heads + h) * (B * D) + tile_offset(t, d)
+ *     ((L * num_blocks + b) * num_kv_heads + h) * (2 * B * D) + tile_offset_K(t, d)
  *
- * i.e. the pool is [layer][block][kv_head][tile], one tile = B*D elements (4 KiB for D=128, B=16)
- * and tile bases are 4 KiB aligned when the pool base is. Inside a tile, the B tokens are split
+ * and the value element at the same index plus B * D, with tile_offset_V. So the K and V tiles of
+ * one (block, kv head) are one contiguous region of 2 * B * D elements (8 KiB for D=128, B=16),
+ * and a block's region in one layer (all kv heads) is contiguous too. Tile bases are 4 KiB
+ * aligned when the pool base is. The kernels take one layer's K and V *planes*: k_pool points at
+ * the K tile of (block 0, head 0) of that layer and v_pool at its V tile (kv_pool_layer gives
+ * both; v_pool = k_pool + B * D elements), and in each plane the tile of (b, h) starts
+ * 2 * (b * num_kv_heads + h) tiles from the plane's base.
+ * Inside a tile, the B tokens are split
  * into sub-tiles of 16 tokens (sub = t / 16, u = t % 16), each 16*D elements; within a sub-tile:
  *
  *   K tile:  k_off(u, d) = (d / 8) * 128 + u * 8 + (d % 8)
@@ -55,7 +62,7 @@
  *   V tile:  v_off(u, d) = ((((d / 32) * 4 + u / 4) * 16 + d % 16) * 2 + (d / 16) % 2) * 4 + u % 4
  *            -> [D/32][4 token quads][16 dims][2 dim halves][4 tokens]: four consecutive tokens of
  *               one dim are one 8-byte chunk.
- *   tile_offset(t, d) = (t / 16) * 16 * D + {k_off | v_off}(t % 16, d)
+ *   tile_offset_K(t, d) = (t / 16) * 16 * D + k_off(t % 16, d)   (tile_offset_V: v_off)
  *
  * Worked examples (D = 128, B = 16): K (t=1,d=0) -> 8; K (t=0,d=8) -> 128; K (t=5,d=37) -> 557;
  * V (t=1,d=0) -> 1; V (t=0,d=1) -> 8; V (t=0,d=16) -> 4; V (t=5,d=37) -> 681;
@@ -66,8 +73,8 @@
  *
  * A slot is `physical_block * block_size + t` (token slot t of that block).
  *
- * fp8 pools (PKV_FP8_E4M3) use the same [layer][block][kv_head][tile] order and 16-token
- * sub-tiles, one byte per element, with these orders inside a sub-tile (byte offsets):
+ * fp8 pools (PKV_FP8_E4M3) use the same [layer][block][kv_head][K tile, V tile] order and
+ * 16-token sub-tiles, one byte per element, with these orders inside a sub-tile (byte offsets):
  *   K8 tile: k8_off(u, d) = (d / 64) * 1024 + (16 * ((d / 8) % 4) + u) * 16 + ((d / 32) % 2) * 8
  *                           + d % 8
  *   V8 tile: v8_off(u, d) = (d / 64) * 1024 + ((u / 4) * 16 + d % 16) * 16 + ((d / 16) % 4) * 4
@@ -103,33 +110,33 @@ typedef enum {
  * q), or E4M3 codes (PKV_FP8_E4M3, see reshape_and_cache_fp8 / paged_attention_decode_fp8). */
 typedef enum { PKV_BF16 = 0, PKV_FP16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
-/* Opaque host-side description of one K pool and one V pool holding every layer. */
+/* Opaque host-side description of one KV pool holding K and V of every layer. */
 typedef struct pkv_pool pkv_pool;
 
 /*
- * Bytes of ONE of the two pools (K or V) for all layers:
- *   num_layers * num_blocks * num_kv_heads * block_size * head_dim * element bytes
+ * Bytes of the pool (K and V of all layers):
+ *   2 * num_layers * num_blocks * num_kv_heads * block_size * head_dim * element bytes
  * (2 for bf16/fp16, 1 for PKV_FP8_E4M3).
  * This is the per-token KV size of the sizing formula ("KV-Cache Management and PagedAttention",
  * section "Why the cache exists, and why it's so hungry"; "PagedAttention and KV Cache
- * Management", section "The KV Cache Size Equation"), halved because K and V are separate pools,
- * times block_size * num_blocks tokens. Returns 0 for any non-positive argument, an
- * unsupported shape, or on size_t overflow.
+ * Management", section "The KV Cache Size Equation") times block_size * num_blocks tokens.
+ * Returns 0 for any non-positive argument, an unsupported shape, or on size_t overflow.
  */
 size_t kv_pool_bytes(int num_layers, int num_blocks, int num_kv_heads, int head_dim, int block_size,
                      pkv_dtype dtype);
 
 /*
- * Describe caller-allocated K and V pools (device memory, `bytes_each` bytes each, laid out as
- * above). Checks: non-NULL, 256-byte aligned bases, bytes_each >= kv_pool_bytes(...), supported
- * shape. On success *out receives a new host object (free it with kv_pool_destroy). The device
- * memory stays owned by the caller and must outlive the object. No device work is done.
+ * Describe a caller-allocated pool (`bytes` bytes at `base`, laid out as above). Checks:
+ * non-NULL, 256-byte aligned base, bytes >= kv_pool_bytes(...), supported shape. On success *out
+ * receives a new host object (free it with kv_pool_destroy). The memory stays owned by the caller
+ * and must outlive the object. No device work is done.
  */
-pkv_status kv_pool_create(pkv_pool** out, void* k_base, void* v_base, size_t bytes_each,
-                          int num_layers, int num_blocks, int num_kv_heads, int head_dim,
-                          int block_size, pkv_dtype dtype);
+pkv_status kv_pool_create(pkv_pool** out, void* base, size_t bytes, int num_layers,
+                          int num_blocks, int num_kv_heads, int head_dim, int block_size,
+                          pkv_dtype dtype);
 
-/* Device addresses of layer `layer`'s K and V sub-pools ([num_blocks][num_kv_heads][tile]). */
+/* Addresses of layer `layer`'s K and V planes: k_layer = base + layer * (kv_pool_bytes / layers),
+ * v_layer = k_layer + one tile (block_size * head_dim elements). */
 pkv_status kv_pool_layer(const pkv_pool* pool, int layer, void** k_layer, void** v_layer);
 
 /* Frees the host object (NULL is a no-op). Does not touch device memory. */
@@ -145,9 +152,9 @@ void kv_pool_destroy(pkv_pool* pool);
  * writes the token there ("PagedAttention and KV Cache Management", section "How Block Paging
  * Operates During Generation").
  *   key, value    device, [num_tokens][num_kv_heads][head_dim], contiguous, 16-byte aligned.
- *   k_pool,v_pool device, ONE layer's sub-pool (kv_pool_layer), 16-byte aligned.
+ *   k_pool,v_pool device, ONE layer's K and V planes (kv_pool_layer), 16-byte aligned.
  *   slot_mapping  device int64 [num_tokens]; distinct slots. A slot >= num_blocks*block_size is
- *                 skipped like a negative one (nothing is written outside the sub-pool).
+ *                 skipped like a negative one (nothing is written outside the layer's region).
  * num_tokens == 0 is a no-op returning PKV_OK.
  */
 pkv_status reshape_and_cache(const void* key, const void* value, void* k_pool, void* v_pool,
@@ -165,7 +172,7 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* k_pool, v
  * and KV Cache Management", section "The KV Cache Size Equation"); the format and the per-pool
  * scale are this library's choice.
  *   key, value    device, [num_tokens][num_kv_heads][head_dim] of src_dtype (bf16 or fp16).
- *   k_pool,v_pool device, ONE layer's fp8 sub-pool (1 byte per element, layout above).
+ *   k_pool,v_pool device, ONE layer's fp8 K and V planes (1 byte per element, layout above).
  *   k_scale, v_scale  finite, > 0.
  * Otherwise as reshape_and_cache.
  */
@@ -210,7 +217,7 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  * ceil(n / B) are never used, whatever they hold (NaN included).
  *   out          device, [num_seqs][num_q_heads][head_dim], same dtype as q.
  *   q            device, [num_seqs][num_q_heads][head_dim], contiguous, 16-byte aligned.
- *   k_pool/v_pool ONE layer's sub-pools (kv_pool_layer), 16-byte aligned.
+ *   k_pool/v_pool ONE layer's K and V planes (kv_pool_layer), 16-byte aligned.
  *   block_tables device int32 [num_seqs][max_blocks_per_seq].
  *   context_lens device int32 [num_seqs], each in [0, min(max_context_len, max_blocks_per_seq*B)].
  *   scale        multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
@@ -235,8 +242,8 @@ pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, 
 
 /*
  * Copy-on-write block copies: for each i in [0, num_copies), block src_blocks[i] is copied to
- * block dst_blocks[i] in the K and the V pool of every layer of `pool` (all kv heads, all
- * block_size token slots), bit-exact. This is the device half of copy-on-write ("PagedAttention
+ * block dst_blocks[i] in every layer of `pool` (K and V, all kv heads, all block_size token
+ * slots: one contiguous region per layer), bit-exact. This is the device half of copy-on-write ("PagedAttention
  * and KV Cache Management" (blog.sejan.dev), section "Advanced Memory Sharing: Prefix Caching &
  * Copy-on-Write", part 2: a fresh block receives a copy of the shared block before the writer's
  * table points at it). Run it before the reshape_and_cache that writes into the copies.
@@ -392,7 +399,7 @@ pkv_status paged_attention_decode_fp8(void* out, const void* q, const void* k_po
  *   key, value   device, [num_seqs][num_kv_heads][head_dim] of dtype: row s is the K / V of
  *                sequence s's token at position context_lens[s] - 1, the step's new token.
  *                Ignored for sequences with context length 0.
- *   k_pool, v_pool  one layer's sub-pools; the new token is written into its slot
+ *   k_pool, v_pool  one layer's K and V planes; the new token is written into its slot
  *                (block_tables[s][(n - 1) / block_size] * block_size + (n - 1) % block_size,
  *                bit-exact as reshape_and_cache writes it) by the workgroup that reads that
  *                slot's tile, before it reads anything, and then attended to like every other

@@ -57,7 +57,7 @@ def load_library(build_if_missing: bool = True):
     vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     lib.kv_pool_bytes.argtypes = [i, i, i, i, i, i]
     lib.kv_pool_bytes.restype = sz
-    lib.kv_pool_create.argtypes = [ctypes.POINTER(vp), vp, vp, sz, i, i, i, i, i, i]
+    lib.kv_pool_create.argtypes = [ctypes.POINTER(vp), vp, sz, i, i, i, i, i, i]
     lib.kv_pool_create.restype = i
     lib.kv_pool_layer.argtypes = [vp, i, ctypes.POINTER(vp), ctypes.POINTER(vp)]
     lib.kv_pool_layer.restype = i
@@ -164,17 +164,18 @@ def kv_pool_bytes(num_layers: int, num_blocks: int, num_kv_heads: int, head_dim:
 
 
 class KVPool:
-    """Host-side geometry of caller-owned K and V pools (kv_pool_create / kv_pool_destroy)."""
+    """Host-side geometry of a caller-owned KV pool (kv_pool_create / kv_pool_destroy): one
+    allocation of [layer][block][kv_head][K tile, V tile]."""
 
-    def __init__(self, k_base, v_base, bytes_each: int, num_layers: int, num_blocks: int,
-                 num_kv_heads: int, head_dim: int, block_size: int, dtype: int):
+    def __init__(self, base, nbytes: int, num_layers: int, num_blocks: int, num_kv_heads: int,
+                 head_dim: int, block_size: int, dtype: int):
         lib = load_library()
         h = ctypes.c_void_p()
-        _check("kv_pool_create", lib.kv_pool_create(ctypes.byref(h), _ptr(k_base), _ptr(v_base),
-                                                    bytes_each, num_layers, num_blocks,
-                                                    num_kv_heads, head_dim, block_size, dtype))
+        _check("kv_pool_create", lib.kv_pool_create(ctypes.byref(h), _ptr(base), nbytes,
+                                                    num_layers, num_blocks, num_kv_heads,
+                                                    head_dim, block_size, dtype))
         self._h = h
-        self._keep = (k_base, v_base)
+        self._keep = base
         self.num_layers = num_layers
 
     def layer(self, layer: int) -> Tuple[int, int]:
@@ -192,10 +193,9 @@ class KVPool:
             pass
 
 
-def kv_pool_create(k_base, v_base, bytes_each: int, num_layers: int, num_blocks: int,
-                   num_kv_heads: int, head_dim: int, block_size: int, dtype: int) -> KVPool:
-    return KVPool(k_base, v_base, bytes_each, num_layers, num_blocks, num_kv_heads, head_dim,
-                  block_size, dtype)
+def kv_pool_create(base, nbytes: int, num_layers: int, num_blocks: int, num_kv_heads: int,
+                   head_dim: int, block_size: int, dtype: int) -> KVPool:
+    return KVPool(base, nbytes, num_layers, num_blocks, num_kv_heads, head_dim, block_size, dtype)
 
 
 def kv_pool_layer(pool: KVPool, layer: int) -> Tuple[int, int]:
@@ -212,7 +212,7 @@ def kv_pool_destroy(pool: KVPool) -> None:
 def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, num_blocks: int,
                       block_size: int = 16, stream=None) -> None:
     """Scatter key/value [T][Hkv][D] into the pool slots named by slot_mapping (int64 [T]).
-    k_pool / v_pool: one layer's sub-pool, as a tensor or a device address."""
+    k_pool / v_pool: one layer's K and V planes, as tensors (views) or device addresses."""
     _require_cuda(key, value, k_pool, v_pool, slot_mapping)
     T, Hkv, D = key.shape
     _check("reshape_and_cache", load_library().reshape_and_cache(

@@ -11,8 +11,8 @@
 #include "pkv_internal.h"
 
 struct pkv_pool {
-  char* k;
-  char* v;
+  char* base;             // layer 0, block 0, kv head 0: its K tile, then its V tile
+  size_t tile_bytes;      // one (block, kv head) tile of K or of V
   size_t layer_bytes;
   int num_layers;
   int num_blocks;
@@ -94,9 +94,9 @@ int odd_xcd_weight() {
   return v < pkv::kEvenWeight / 2 ? pkv::kEvenWeight / 2 : v > pkv::kEvenWeight ? pkv::kEvenWeight : v;
 }
 
-// Bytes of one block's region in one layer of one of the two pools.
+// Bytes of one block's region in one layer: the K and V tiles of all its kv heads.
 size_t block_bytes_of(const pkv_pool* p) {
-  return (size_t)p->num_kv_heads * p->block_size * p->head_dim * elem_bytes(p->dtype);
+  return (size_t)p->num_kv_heads * 2 * p->tile_bytes;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -182,7 +182,7 @@ size_t kv_pool_bytes(int num_layers, int num_blocks, int num_kv_heads, int head_
                      int block_size, pkv_dtype dtype) {
   if (num_layers <= 0 || num_blocks <= 0 || num_kv_heads <= 0) return 0;
   if (!supported_pool(head_dim, block_size, dtype)) return 0;
-  size_t r = elem_bytes(dtype);
+  size_t r = 2 * elem_bytes(dtype);  // K and V
   const size_t f[5] = {(size_t)num_layers, (size_t)num_blocks, (size_t)num_kv_heads,
                        (size_t)block_size, (size_t)head_dim};
   for (size_t x : f) {
@@ -191,22 +191,22 @@ size_t kv_pool_bytes(int num_layers, int num_blocks, int num_kv_heads, int head_
   return r;
 }
 
-pkv_status kv_pool_create(pkv_pool** out, void* k_base, void* v_base, size_t bytes_each,
-                          int num_layers, int num_blocks, int num_kv_heads, int head_dim,
-                          int block_size, pkv_dtype dtype) {
+pkv_status kv_pool_create(pkv_pool** out, void* base, size_t bytes, int num_layers,
+                          int num_blocks, int num_kv_heads, int head_dim, int block_size,
+                          pkv_dtype dtype) {
   if (out == nullptr) return PKV_ERR_INVALID_ARG;
   *out = nullptr;
-  if (k_base == nullptr || v_base == nullptr) return PKV_ERR_INVALID_ARG;
+  if (base == nullptr) return PKV_ERR_INVALID_ARG;
   if (num_layers <= 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
   if (!supported_pool(head_dim, block_size, dtype)) return PKV_ERR_UNSUPPORTED;
-  if (((uintptr_t)k_base & 255u) || ((uintptr_t)v_base & 255u)) return PKV_ERR_ALIGNMENT;
+  if ((uintptr_t)base & 255u) return PKV_ERR_ALIGNMENT;
   const size_t need = kv_pool_bytes(num_layers, num_blocks, num_kv_heads, head_dim, block_size,
                                     dtype);
-  if (need == 0 || bytes_each < need) return PKV_ERR_INVALID_ARG;
+  if (need == 0 || bytes < need) return PKV_ERR_INVALID_ARG;
   pkv_pool* p = (pkv_pool*)malloc(sizeof(pkv_pool));
   if (p == nullptr) return PKV_ERR_INVALID_ARG;
-  p->k = (char*)k_base;
-  p->v = (char*)v_base;
+  p->base = (char*)base;
+  p->tile_bytes = (size_t)block_size * head_dim * elem_bytes(dtype);
   p->layer_bytes = need / (size_t)num_layers;
   p->num_layers = num_layers;
   p->num_blocks = num_blocks;
@@ -221,8 +221,9 @@ pkv_status kv_pool_create(pkv_pool** out, void* k_base, void* v_base, size_t byt
 pkv_status kv_pool_layer(const pkv_pool* pool, int layer, void** k_layer, void** v_layer) {
   if (pool == nullptr || k_layer == nullptr || v_layer == nullptr) return PKV_ERR_INVALID_ARG;
   if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_INVALID_ARG;
-  *k_layer = pool->k + (size_t)layer * pool->layer_bytes;
-  *v_layer = pool->v + (size_t)layer * pool->layer_bytes;
+  char* k = pool->base + (size_t)layer * pool->layer_bytes;
+  *k_layer = k;
+  *v_layer = k + pool->tile_bytes;
   return PKV_OK;
 }
 
@@ -276,10 +277,8 @@ pkv_status copy_blocks(const pkv_pool* pool, const int32_t* src_blocks, const in
   if (!device_visible(src_blocks, &src_dev) || !device_visible(dst_blocks, &dst_dev))
     return PKV_ERR_INVALID_ARG;
   pkv::BlockCopy c;
-  c.src_k = pool->k;
-  c.src_v = pool->v;
-  c.dst_k = pool->k;
-  c.dst_v = pool->v;
+  c.src = pool->base;
+  c.dst = pool->base;
   c.src_layer_bytes = c.dst_layer_bytes = pool->layer_bytes;
   c.block_bytes = block_bytes_of(pool);
   c.src_ids = src_dev;
@@ -307,20 +306,16 @@ pkv_status swap_blocks(const pkv_pool* device_pool, const pkv_pool* host_pool,
   // The host pool must be pinned, device-mapped memory: refuse anything else instead of letting
   // the kernel fault on it, and use the device addresses of its bases.
   const size_t host_bytes = h.layer_bytes * (size_t)h.num_layers;
-  void* hk = nullptr;
-  void* hv = nullptr;
-  if (!pinned_device_address(h.k, host_bytes, &hk) || !pinned_device_address(h.v, host_bytes, &hv))
-    return PKV_ERR_INVALID_ARG;
+  void* hbase = nullptr;
+  if (!pinned_device_address(h.base, host_bytes, &hbase)) return PKV_ERR_INVALID_ARG;
   const int32_t* src_dev = nullptr;
   const int32_t* dst_dev = nullptr;
   if (!device_visible(src_blocks, &src_dev) || !device_visible(dst_blocks, &dst_dev))
     return PKV_ERR_INVALID_ARG;
   pkv::BlockCopy c;
   const bool out = direction == PKV_SWAP_OUT;
-  c.src_k = out ? d.k : (const char*)hk;
-  c.src_v = out ? d.v : (const char*)hv;
-  c.dst_k = out ? (char*)hk : d.k;
-  c.dst_v = out ? (char*)hv : d.v;
+  c.src = out ? d.base : (const char*)hbase;
+  c.dst = out ? (char*)hbase : d.base;
   c.src_layer_bytes = out ? d.layer_bytes : h.layer_bytes;
   c.dst_layer_bytes = out ? h.layer_bytes : d.layer_bytes;
   c.block_bytes = block_bytes_of(&d);

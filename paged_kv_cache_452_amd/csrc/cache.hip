@@ -34,8 +34,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int64_t b = slot / block_size;
   const int tb = (int)(slot % block_size);
   const int t = tb % kBlock;  // token within its 16-token sub-tile
-  // tile of (block, kv head), then the sub-tile holding the token
-  const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)block_size * D +
+  // tile of (block, kv head) in its plane (K and V tiles alternate: a stride of two tiles), then
+  // the sub-tile holding the token
+  const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)(2 * block_size) * D +
                       (size_t)(tb / kBlock) * (kBlock * D);
   const size_t src = ((size_t)i * num_kv_heads + h) * D + 8 * c;
 
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   const int64_t b = slot / block_size;
   const int tb = (int)(slot % block_size);
   const int t = tb % kBlock;
-  const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)block_size * D +
+  const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)(2 * block_size) * D +
                       (size_t)(tb / kBlock) * (kBlock * D);
   const size_t src = ((size_t)i * num_kv_heads + h) * D + 8 * c;
   const u32x4 kw = *(const u32x4*)(key + src);
@@ -112,12 +113,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
 }
 
 // Whole-block copies between two pools of one geometry: the same device pool (copy-on-write),
-// or a device pool and a pinned host pool (swapping). For pair i and layer L, the K and V regions
-// of block src[i] of the source (all kv heads, all token slots: block_bytes each) are copied to
+// or a device pool and a pinned host pool (swapping). For pair i and layer L, the region of block
+// src[i] of the source (the K and V tiles of all kv heads: block_bytes, contiguous) is copied to
 // block dst[i] of the destination. One thread moves 16 bytes; the grid is (16-byte chunks of a
-// region / 256, pairs, layers * 2 (K, V)), so consecutive workgroups stream consecutive 4 KiB of
-// one region. A pair with an id outside its pool is skipped. Pure streaming copy. (Measured on
-// device pools: one workgroup per region with 8 loads in flight per thread was 15% slower.)
+// region / 256, pairs, layers), so consecutive workgroups stream consecutive 4 KiB of one region.
+// A pair with an id outside its pool is skipped. Pure streaming copy. (Measured on device pools:
+// one workgroup per region with 8 loads in flight per thread was 15% slower.)
 __global__ __launch_bounds__(256) void block_copy_kernel(BlockCopy c) {
   const size_t chunk = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (chunk * 16 >= c.block_bytes) return;
@@ -125,12 +126,9 @@ __global__ __launch_bounds__(256) void block_copy_kernel(BlockCopy c) {
   const int s = c.src_ids[i];
   const int d = c.dst_ids[i];
   if (s < 0 || s >= c.src_blocks || d < 0 || d >= c.dst_blocks) return;
-  const int layer = blockIdx.z >> 1;
-  const bool is_v = blockIdx.z & 1;
-  const char* src = (is_v ? c.src_v : c.src_k) + (size_t)layer * c.src_layer_bytes +
-                    (size_t)s * c.block_bytes + chunk * 16;
-  char* dst = (is_v ? c.dst_v : c.dst_k) + (size_t)layer * c.dst_layer_bytes +
-              (size_t)d * c.block_bytes + chunk * 16;
+  const int layer = blockIdx.z;
+  const char* src = c.src + (size_t)layer * c.src_layer_bytes + (size_t)s * c.block_bytes + chunk * 16;
+  char* dst = c.dst + (size_t)layer * c.dst_layer_bytes + (size_t)d * c.block_bytes + chunk * 16;
   const u32x4 w = __builtin_nontemporal_load((const u32x4*)src);
   __builtin_nontemporal_store(w, (u32x4*)dst);
 }
@@ -141,7 +139,7 @@ hipError_t launch_block_copy(const BlockCopy& c, int num_layers, int num_pairs,
                              hipStream_t stream) {
   if (num_pairs == 0) return hipSuccess;
   const size_t chunks = c.block_bytes / 16;
-  const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)num_pairs, (unsigned)(2 * num_layers));
+  const dim3 grid((unsigned)((chunks + 255) / 256), (unsigned)num_pairs, (unsigned)num_layers);
   hipLaunchKernelGGL(block_copy_kernel, grid, dim3(256), 0, stream, c);
   return hipGetLastError();
 }

@@ -34,7 +34,8 @@
 // A stream that lies wholly inside the range is normalised and stored. A stream cut by a range
 // boundary leaves an fp32 partial (m, l, O) in the workspace; the last of its workgroups to finish
 // (an agent-scope counter, reset by that workgroup) merges all of them in range order, so the
-// result does not depend on which workgroup came last.
+// result does not depend on which workgroup came last. A range's first stream, cut at its start,
+// is counted as soon as it ends; the stream cut at the range's end is counted after the loop.
 //
 // Variants (template parameters): head dim 64 or 128; bf16 or fp16 q/out; 16-bit pools or fp8
 // (E4M3) pools whose codes are widened to the q type in registers, with the pool scales folded
@@ -69,12 +70,12 @@ constexpr float kLazyRescale = 8.0f;
 // q rows (query heads) a workgroup stages in LDS for the first streams of its range.
 constexpr int kQRows = 64;
 // Parts whose loads one merge round issues together.
-constexpr int kMergeRound = 8;
+constexpr int kMergeRound = 4;
 
 // Tile buffers per wavefront (blocks in flight = kRing - 1), sized to stay within 256 VGPRs so
-// two workgroups fit on each compute unit. (fp8 tiles hold half the bytes, but a deeper ring for
-// them does not fit: 5 or 6 slots at d128 spill.)
-template <int D, bool KV8, bool APPEND>
+// two workgroups fit on each compute unit. The same for fp8 tiles, which hold half the bytes:
+// 5 or 6 slots spill at d128, and 8 slots fit but measured no faster.
+template <int D>
 constexpr int kRing = D == 128 ? 4 : 8;
 
 template <bool BF16>
@@ -165,7 +166,6 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // that, where the paths join, only the ring's tile loads are outstanding and the compiler keeps
 // the exact, deep waits of the common path.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 
 template <int D, bool BF16, bool KV8, bool APPEND, int RING>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void
@@ -352,7 +352,7 @@ paged_decode_kernel(DecodeLaunch a) {
   }
 
   // ---- Tile ids: lane l of window c holds the 16-token sub-tile of this wave's position 64c + l
-  // (its index in units of 16 * D elements of the layer's pool). ----
+  // (its index in units of 16 * D elements of the layer's K or V plane). ----
   const int span = r1 - r0;
   const int mw = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;  // this wave's blocks
   auto window = [&](int c) -> unsigned {
@@ -366,9 +366,11 @@ paged_decode_kernel(DecodeLaunch a) {
     const int j = r - gh * nb;
     const int g = gh / a.head_tiles;
     // 16-token unit j of the stream: sub-tile j % R of physical block block_tables[s][j / R]
-    // (R = block_size / 16 sub-tiles per block, each 16 * D elements of the block's tile).
+    // (R = block_size / 16 sub-tiles per block, each 16 * D elements of the block's tile). Tiles
+    // of one plane lie two apart (the K and V tiles of a (block, head) alternate), so the K and V
+    // sub-tile both sit at this index times 16 * D elements from their plane's base.
     const unsigned b = (unsigned)a.block_tables[(size_t)s * a.max_blocks + (j >> a.sub_shift)];
-    return ((b * (unsigned)a.num_kv_heads + (unsigned)g) << a.sub_shift) +
+    return ((b * (unsigned)a.num_kv_heads + (unsigned)g) << (a.sub_shift + 1)) +
            (unsigned)(j & ((1 << a.sub_shift) - 1));
   };
   unsigned win_a = window(0);
@@ -395,7 +397,7 @@ paged_decode_kernel(DecodeLaunch a) {
           const int tt = p & 15;
           const int d = 2 * lane;
           const size_t tile =
-              ((size_t)((b * (unsigned)a.num_kv_heads + (unsigned)g) << a.sub_shift) +
+              ((size_t)((b * (unsigned)a.num_kv_heads + (unsigned)g) << (a.sub_shift + 1)) +
                (size_t)((p >> 4) & ((1 << a.sub_shift) - 1))) * (kBlock * D);
           if constexpr (KV8) {  // quantized as reshape_and_cache_fp8 does
             const unsigned kc = e4m3_code(E::widen((unsigned short)kw) * a.k_inv) |
@@ -568,11 +570,23 @@ paged_decode_kernel(DecodeLaunch a) {
     if (!complete) {
       if (slot == 0) {
         split0 = cur.start;
+        wait_vmem();  // this wave's share of the partial is at the coherence point
       } else {
         split1 = cur.start;
       }
     }
     if (complete || slot == 0) __syncthreads();  // the combine buffer is free again
+    if (!complete && slot == 0 && tid == 0) {
+      // Every wave has drained its share: count this part now rather than after the main loop,
+      // so that the workgroup finishing the stream's other parts at its range end usually finds
+      // them all in and merges at once. A part that completes the count merges after the loop.
+      const int wa0 = range_owner(cur.start, nwg, W, odd_w);
+      const int np0 = range_owner(cur.end - 1, nwg, W, odd_w) - wa0 + 1;
+      const unsigned old = atomicAdd(a.counters + wa0, 1u);
+      const int last = old == (unsigned)(np0 - 1);
+      if (last) __hip_atomic_store(a.counters + wa0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last[0] = last;
+    }
     cur = nxt;
   };
 
@@ -787,6 +801,7 @@ paged_decode_kernel(DecodeLaunch a) {
   // ---- Publish the split streams (uniform: every wave saw the same ones). ----
   // A split stream's parts are counted on the arrival counter of its first part's workgroup; the
   // part that brings the count to the number of parts merges them all and resets the counter.
+  // Split 0 was counted when its stream ended (s_last[0]); split 1 is counted here.
   const bool has0 = split0 >= 0, has1 = split1 >= 0;
   if (has0 || has1) {
     // The stream starting at flattened position p.
@@ -798,8 +813,6 @@ paged_decode_kernel(DecodeLaunch a) {
     };
     const Stream st0 = stream_from(has0 ? split0 : split1);
     const Stream st1 = stream_from(has1 ? split1 : split0);
-    const int wa0 = range_owner(st0.start, nwg, W, odd_w);
-    const int np0 = range_owner(st0.end - 1, nwg, W, odd_w) - wa0 + 1;
     const int np1 = range_owner(st1.end - 1, nwg, W, odd_w) - wg + 1;  // st1 starts in this range
     // Split 1's own part, folded once from the combine buffer: both ways of finishing it below
     // use these very values, so the result cannot depend on which workgroup arrives last.
@@ -807,14 +820,7 @@ paged_decode_kernel(DecodeLaunch a) {
 #pragma unroll
     for (int i = 0; i < kDims; ++i) acc1[i] = 0.f;
     if (has1 && head < st1.nvalid) combine_waves(m1, l1, acc1);
-    wait_vmem();  // split 0's partial is complete at the coherence point before it is counted
-    __syncthreads();
-    if (tid == 0 && has0) {
-      const unsigned old = atomicAdd(a.counters + wa0, 1u);
-      const int last = old == (unsigned)(np0 - 1);
-      if (last) __hip_atomic_store(a.counters + wa0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last[0] = last;
-    }
+    __syncthreads();  // s_last[0] (set when split 0 ended) is visible
     if (tid == 1 && has1) {
       // Split 1 begins here, so its counter is this workgroup's. When every other part has
       // already arrived, this workgroup is the last: it merges at once, taking its own part from
@@ -850,7 +856,7 @@ paged_decode_kernel(DecodeLaunch a) {
 
 template <int D, bool BF16, bool KV8, bool APPEND>
 hipError_t launch_typed(const DecodeLaunch& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_kernel<D, BF16, KV8, APPEND, kRing<D, KV8, APPEND>>),
+  hipLaunchKernelGGL((paged_decode_kernel<D, BF16, KV8, APPEND, kRing<D>>),
                      dim3((unsigned)grid), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }

@@ -86,8 +86,8 @@ __host__ __device__ inline int range_owner(int p, int nwg, int W, int odd_weight
 struct DecodeLaunch {
   void* out;
   const void* q;
-  const void* k_pool;
-  const void* v_pool;
+  const void* k_pool;   // K and V planes of one layer: the tiles of (block b, kv head g) start
+  const void* v_pool;   // 2 * (b * num_kv_heads + g) tiles into each
   const int32_t* block_tables;
   const int32_t* context_lens;
   unsigned* counters;   // [grid] arrival counts of split streams; zero between launches
@@ -124,18 +124,16 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         int num_blocks, bool src_bf16, float k_inv_scale,
                                         float v_inv_scale, hipStream_t stream);
 
-// Copy the K and V regions of blocks src[i] -> dst[i] in every layer (device arrays).
 // One whole-block copy launch: pair i copies block src_ids[i] of the source pool to block
-// dst_ids[i] of the destination pool, K and V of every layer. Addresses are device-visible (a
-// pinned host pool is passed by its device address).
+// dst_ids[i] of the destination pool in every layer. A block's region in one layer (the K and V
+// tiles of all its kv heads) is contiguous. Addresses are device-visible (a pinned host pool is
+// passed by its device address).
 struct BlockCopy {
-  const char* src_k;
-  const char* src_v;
-  char* dst_k;
-  char* dst_v;
+  const char* src;        // pool bases (layer 0, block 0)
+  char* dst;
   size_t src_layer_bytes;
   size_t dst_layer_bytes;
-  size_t block_bytes;     // one layer's region of one block: num_kv_heads * block_size * D * elem
+  size_t block_bytes;     // one layer's region of one block: num_kv_heads * 2 * block_size * D * elem
   const int32_t* src_ids;
   const int32_t* dst_ids;
   int src_blocks;         // ids outside [0, src_blocks) / [0, dst_blocks) are skipped

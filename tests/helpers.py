@@ -78,6 +78,14 @@ def assert_close(got: torch.Tensor, ref: np.ndarray, what: str = ""):
     return max_abs, rel
 
 
+def set_plane_(plane: torch.Tensor, flat_idx: torch.Tensor, value) -> None:
+    """plane[i] = value for indices into the plane's [blocks][kv heads][tile] order (the oracle's
+    pool_index), on a K or V plane view of an interleaved pool (tiles two apart)."""
+    tile = plane.shape[-1]
+    rows = plane.view(-1, tile)
+    rows[flat_idx // tile, flat_idx % tile] = value
+
+
 def poison_dead_slots_(k_layer: torch.Tensor, v_layer: torch.Tensor, tables, lens,
                        num_kv_heads: int, head_dim: int, block_size: int = 16):
     """Write NaN into the unwritten slots (t >= n) of every sequence's last block, locating
@@ -97,8 +105,8 @@ def poison_dead_slots_(k_layer: torch.Tensor, v_layer: torch.Tensor, tables, len
     if not idx:
         return
     ia = torch.tensor(idx, dtype=torch.long, device=k_layer.device)
-    k_layer.view(-1)[ia[:, 0]] = float("nan")
-    v_layer.view(-1)[ia[:, 1]] = float("nan")
+    set_plane_(k_layer, ia[:, 0], float("nan"))
+    set_plane_(v_layer, ia[:, 1], float("nan"))
 
 
 # ---- fp8 (E4M3) pools ----------------------------------------------------------------------
@@ -153,5 +161,5 @@ def poison_dead_slots8_(k_layer: torch.Tensor, v_layer: torch.Tensor, tables, le
     if not idx:
         return
     ia = torch.tensor(idx, dtype=torch.long, device=k_layer.device)
-    k_layer.view(-1)[ia[:, 0]] = 0x7F
-    v_layer.view(-1)[ia[:, 1]] = 0x7F
+    set_plane_(k_layer, ia[:, 0], 0x7F)
+    set_plane_(v_layer, ia[:, 1], 0x7F)

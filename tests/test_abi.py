@@ -41,14 +41,14 @@ def test_status_strings():
 
 def test_kv_pool_bytes_matches_sizing_formula():
     # 70B-shaped: 80 layers x 16384 blocks x 8 kv heads x 16 x 128, bf16; K and V together
-    each = pkv.kv_pool_bytes(80, 16384, 8, 128, 16, pkv.PKV_BF16)
-    assert 2 * each == sizing.kv_bytes(80, 8, 128, 64 * 4096, 2) == 85899345920
-    assert each == 16384 * sizing.block_bytes(16, 80, 8, 128, 2) // 2
-    assert pkv.kv_pool_bytes(1, 64, 4, 64, 16, pkv.PKV_BF16) == 64 * 4 * 16 * 64 * 2
+    total = pkv.kv_pool_bytes(80, 16384, 8, 128, 16, pkv.PKV_BF16)
+    assert total == sizing.kv_bytes(80, 8, 128, 64 * 4096, 2) == 85899345920
+    assert total == 16384 * sizing.block_bytes(16, 80, 8, 128, 2)
+    assert pkv.kv_pool_bytes(1, 64, 4, 64, 16, pkv.PKV_BF16) == 2 * 64 * 4 * 16 * 64 * 2
     # unsupported shapes and bad sizes give 0
     assert pkv.kv_pool_bytes(1, 64, 4, 96, 16, pkv.PKV_BF16) == 0
     assert pkv.kv_pool_bytes(1, 64, 4, 128, 8, pkv.PKV_BF16) == 0
-    assert pkv.kv_pool_bytes(1, 64, 4, 128, 32, pkv.PKV_BF16) == 64 * 4 * 32 * 128 * 2
+    assert pkv.kv_pool_bytes(1, 64, 4, 128, 32, pkv.PKV_BF16) == 2 * 64 * 4 * 32 * 128 * 2
     assert pkv.kv_pool_bytes(0, 64, 4, 128, 16, pkv.PKV_BF16) == 0
     assert pkv.kv_pool_bytes(1, 64, 4, 128, 16, 7) == 0
     # overflow is detected
@@ -57,24 +57,25 @@ def test_kv_pool_bytes_matches_sizing_formula():
 
 def test_kv_pool_create_and_layers():
     lib = pkv.load_library()
-    each = pkv.kv_pool_bytes(80, 16384, 8, 128, 16, pkv.PKV_BF16)
-    pool = pkv.kv_pool_create(FAKE, FAKE * 2, each, 80, 16384, 8, 128, 16, pkv.PKV_BF16)
+    total = pkv.kv_pool_bytes(80, 16384, 8, 128, 16, pkv.PKV_BF16)
+    pool = pkv.kv_pool_create(FAKE, total, 80, 16384, 8, 128, 16, pkv.PKV_BF16)
     k0, v0 = pool.layer(0)
     k5, v5 = pool.layer(5)
-    assert (k0, v0) == (FAKE, 2 * FAKE)
-    assert k5 - k0 == 5 * each // 80 and v5 - v0 == 5 * each // 80
+    tile = 16 * 128 * 2  # the V plane starts one tile after the K plane
+    assert (k0, v0) == (FAKE, FAKE + tile)
+    assert k5 - k0 == 5 * total // 80 and v5 - k5 == tile
     with pytest.raises(pkv.PagedKVError):
         pool.layer(80)
     with pytest.raises(pkv.PagedKVError):
         pool.layer(-1)
     pool.destroy()
     h = ctypes.c_void_p()
-    assert lib.kv_pool_create(ctypes.byref(h), FAKE + 16, FAKE, each, 80, 16384, 8, 128, 16, 0) == ALIGN
+    assert lib.kv_pool_create(ctypes.byref(h), FAKE + 16, total, 80, 16384, 8, 128, 16, 0) == ALIGN
     assert h.value is None
-    assert lib.kv_pool_create(ctypes.byref(h), FAKE, FAKE, each - 1, 80, 16384, 8, 128, 16, 0) == INVALID
-    assert lib.kv_pool_create(ctypes.byref(h), None, FAKE, each, 80, 16384, 8, 128, 16, 0) == INVALID
-    assert lib.kv_pool_create(ctypes.byref(h), FAKE, FAKE, each, 80, 16384, 8, 96, 16, 0) == UNSUPPORTED
-    assert lib.kv_pool_create(None, FAKE, FAKE, each, 80, 16384, 8, 128, 16, 0) == INVALID
+    assert lib.kv_pool_create(ctypes.byref(h), FAKE, total - 1, 80, 16384, 8, 128, 16, 0) == INVALID
+    assert lib.kv_pool_create(ctypes.byref(h), None, total, 80, 16384, 8, 128, 16, 0) == INVALID
+    assert lib.kv_pool_create(ctypes.byref(h), FAKE, total, 80, 16384, 8, 96, 16, 0) == UNSUPPORTED
+    assert lib.kv_pool_create(None, FAKE, total, 80, 16384, 8, 128, 16, 0) == INVALID
     lib.kv_pool_destroy(None)
 
 
@@ -165,8 +166,8 @@ def test_binding_refuses_host_tensors():
 
 def test_copy_blocks_argument_errors():
     lib = pkv.load_library()
-    each = pkv.kv_pool_bytes(2, 16, 4, 128, 16, pkv.PKV_BF16)
-    pool = pkv.kv_pool_create(FAKE, FAKE * 2, each, 2, 16, 4, 128, 16, pkv.PKV_BF16)
+    total = pkv.kv_pool_bytes(2, 16, 4, 128, 16, pkv.PKV_BF16)
+    pool = pkv.kv_pool_create(FAKE, total, 2, 16, 4, 128, 16, pkv.PKV_BF16)
     f = lib.copy_blocks
     assert f(pool._h, None, None, 0, None) == OK            # nothing to copy, nothing launched
     assert f(None, FAKE, FAKE, 1, None) == INVALID
@@ -180,12 +181,12 @@ def test_copy_blocks_argument_errors():
 def test_fp8_pool_sizing_and_argument_errors():
     lib = pkv.load_library()
     FP8 = pkv.PKV_FP8_E4M3
-    each = pkv.kv_pool_bytes(80, 16384, 8, 128, 16, FP8)
-    assert 2 * each == sizing.kv_bytes(80, 8, 128, 64 * 4096, 1)
-    assert each == pkv.kv_pool_bytes(80, 16384, 8, 128, 16, pkv.PKV_BF16) // 2
-    pool = pkv.kv_pool_create(FAKE, FAKE * 2, each, 80, 16384, 8, 128, 16, FP8)
-    k1, _ = pool.layer(1)
-    assert k1 - FAKE == 16384 * 8 * 16 * 128
+    total = pkv.kv_pool_bytes(80, 16384, 8, 128, 16, FP8)
+    assert total == sizing.kv_bytes(80, 8, 128, 64 * 4096, 1)
+    assert total == pkv.kv_pool_bytes(80, 16384, 8, 128, 16, pkv.PKV_BF16) // 2
+    pool = pkv.kv_pool_create(FAKE, total, 80, 16384, 8, 128, 16, FP8)
+    k1, v1 = pool.layer(1)
+    assert k1 - FAKE == 2 * 16384 * 8 * 16 * 128 and v1 - k1 == 16 * 128
     pool.destroy()
 
     r = lib.reshape_and_cache_fp8
@@ -227,12 +228,12 @@ def test_fp8_pool_sizing_and_argument_errors():
 
 def test_swap_blocks_argument_errors():
     lib = pkv.load_library()
-    each = pkv.kv_pool_bytes(2, 16, 4, 128, 16, pkv.PKV_BF16)
-    dev = pkv.kv_pool_create(FAKE, FAKE * 2, each, 2, 16, 4, 128, 16, pkv.PKV_BF16)
-    each_h = pkv.kv_pool_bytes(2, 8, 4, 128, 16, pkv.PKV_BF16)
-    host = pkv.kv_pool_create(FAKE * 3, FAKE * 4, each_h, 2, 8, 4, 128, 16, pkv.PKV_BF16)
-    other = pkv.kv_pool_create(FAKE * 3, FAKE * 4, each_h, 2, 8, 4, 64, 16, pkv.PKV_BF16)
-    fp8 = pkv.kv_pool_create(FAKE * 3, FAKE * 4, each_h, 2, 8, 4, 128, 16, pkv.PKV_FP8_E4M3)
+    total = pkv.kv_pool_bytes(2, 16, 4, 128, 16, pkv.PKV_BF16)
+    dev = pkv.kv_pool_create(FAKE, total, 2, 16, 4, 128, 16, pkv.PKV_BF16)
+    total_h = pkv.kv_pool_bytes(2, 8, 4, 128, 16, pkv.PKV_BF16)
+    host = pkv.kv_pool_create(FAKE * 3, total_h, 2, 8, 4, 128, 16, pkv.PKV_BF16)
+    other = pkv.kv_pool_create(FAKE * 3, total_h, 2, 8, 4, 64, 16, pkv.PKV_BF16)
+    fp8 = pkv.kv_pool_create(FAKE * 3, total_h, 2, 8, 4, 128, 16, pkv.PKV_FP8_E4M3)
     f = lib.swap_blocks
     assert f(dev._h, host._h, None, None, 0, 0, None) == OK      # nothing to copy
     assert f(dev._h, host._h, None, None, 0, 1, None) == OK

@@ -33,11 +33,11 @@ def _host_copy_blocks(k_words, v_words, pairs):
                                               (80, 64, 8, 128, torch.bfloat16)])
 def test_copy_blocks_whole_pool_bit_exact(L, NB, Hkv, D, dtype):
     g = torch.Generator(device=DEV).manual_seed(L * 1000 + NB)
-    shape = (L, NB, Hkv, 16 * D)
-    k = workloads.randn(shape, dtype, g, DEV)
-    v = workloads.randn(shape, dtype, g, DEV)
+    kv = workloads.new_pool(L, NB, Hkv, 16, D, dtype, DEV)
+    kv.copy_(workloads.randn(tuple(kv.shape), dtype, g, DEV))
+    k, v = workloads.planes(kv)
     dt = pkv.PKV_BF16 if dtype == torch.bfloat16 else pkv.PKV_FP16
-    pool = pkv.kv_pool_create(k, v, k.numel() * 2, L, NB, Hkv, D, 16, dt)
+    pool = pkv.kv_pool_create(kv, kv.numel() * 2, L, NB, Hkv, D, 16, dt)
     rng = np.random.default_rng(NB)
     perm = rng.permutation(NB)
     n = NB // 3
@@ -61,9 +61,9 @@ def test_fork_copy_on_write_decode_step():
     Hq, Hkv, D, B, NB = 16, 4, 128, 16, 48
     dt = torch.bfloat16
     g = torch.Generator(device=DEV).manual_seed(77)
-    k = torch.full((NB, Hkv, B * D), float("nan"), dtype=dt, device=DEV)
-    v = torch.full((NB, Hkv, B * D), float("nan"), dtype=dt, device=DEV)
-    pool = pkv.kv_pool_create(k, v, k.numel() * 2, 1, NB, Hkv, D, B, pkv.PKV_BF16)
+    kv = workloads.new_pool(1, NB, Hkv, B, D, dt, DEV).fill_(float("nan"))
+    k, v = (x[0] for x in workloads.planes(kv))
+    pool = pkv.kv_pool_create(kv, kv.numel() * 2, 1, NB, Hkv, D, B, pkv.PKV_BF16)
     bm = pkv.BlockManager(NB, B)
     n0 = 37                                    # 3 blocks, the last one 5/16 full
     bm.allocate(0, n0)

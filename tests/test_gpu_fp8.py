@@ -11,7 +11,8 @@ import torch
 import oracle
 import paged_kv_cache_452_amd as pkv
 import workloads
-from helpers import (assert_close, codes, gpu_decode8, oracle_decode8, poison_dead_slots8_, say)
+from helpers import (assert_close, codes, gpu_decode8, oracle_decode8, poison_dead_slots8_, say,
+                     set_plane_)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -205,11 +206,9 @@ def test_fp8_config4_80_layers_sampled():
 def test_copy_blocks_fp8_pool_bit_exact():
     L, NB, Hkv, D = 4, 50, 8, 128
     g = torch.Generator(device=DEV).manual_seed(5)
-    k = workloads.fill_pool_fp8_(torch.empty((L, NB, Hkv, 16 * D), dtype=torch.uint8, device=DEV),
-                                 g)
-    v = workloads.fill_pool_fp8_(torch.empty((L, NB, Hkv, 16 * D), dtype=torch.uint8, device=DEV),
-                                 g)
-    pool = pkv.kv_pool_create(k, v, k.numel(), L, NB, Hkv, D, 16, pkv.PKV_FP8_E4M3)
+    kv = workloads.fill_pool_fp8_(workloads.new_pool(L, NB, Hkv, 16, D, torch.uint8, DEV), g)
+    k, v = workloads.planes(kv)
+    pool = pkv.kv_pool_create(kv, kv.numel(), L, NB, Hkv, D, 16, pkv.PKV_FP8_E4M3)
     rng = np.random.default_rng(50)
     perm = rng.permutation(NB)
     pairs = np.stack([perm[:16], perm[16:32]], axis=1).astype(np.int32)
@@ -242,8 +241,8 @@ def test_fused_append_decode_fp8_matches_oracle(Hq, Hkv, D, lens, B, nwg):
                 idx.append((oracle.pool_index8(False, blk, h, (n - 1) % B, d, Hkv, B, D),
                             oracle.pool_index8(True, blk, h, (n - 1) % B, d, Hkv, B, D)))
     ia = torch.tensor(idx, dtype=torch.long, device=DEV)
-    k.view(-1)[ia[:, 0]] = 0x7F
-    v.view(-1)[ia[:, 1]] = 0x7F
+    set_plane_(k, ia[:, 0], 0x7F)
+    set_plane_(v, ia[:, 1], 0x7F)
     kb, vb = codes(k), codes(v)
     oracle.reshape_and_cache8(kb, vb, b.new_key.cpu(), b.new_value.cpu(), oracle.BF16, ks, vs,
                               t.slot_mapping, Hkv, D, B, t.num_blocks)

@@ -41,9 +41,9 @@ def test_physical_block_permutation_gives_identical_output():
     k, v = b.k_pool[0], b.v_pool[0]
     base = _run(spec, b, k, v, b.block_tables)
     perm = torch.from_numpy(rng.permutation(t.num_blocks)).to(DEV)
-    k2, v2 = torch.empty_like(k), torch.empty_like(v)
-    k2[perm] = k
-    v2[perm] = v
+    kv2 = torch.empty_like(b.kv_pool[0])     # [blocks][kv heads][K, V][tile]
+    kv2[perm] = b.kv_pool[0]
+    k2, v2 = kv2.select(-2, 0), kv2.select(-2, 1)
     bt = b.block_tables.clone()
     valid = bt >= 0
     bt[valid] = perm[bt[valid].long()].int()
@@ -63,8 +63,9 @@ def test_shared_prefix_equals_private_copies():
     say("shared prefix")
     shared = _run(spec, b, k, v, b.block_tables)
     prefix = torch.from_numpy(t.block_tables[0, :P].astype(np.int64)).to(DEV)
-    k2 = torch.cat([k, k[prefix].repeat(49, 1, 1)])
-    v2 = torch.cat([v, v[prefix].repeat(49, 1, 1)])
+    kv = b.kv_pool[0]
+    kv2 = torch.cat([kv, kv[prefix].repeat(49, 1, 1, 1)])
+    k2, v2 = kv2.select(-2, 0), kv2.select(-2, 1)
     bt = b.block_tables.clone()
     for s in range(1, 50):
         base = t.num_blocks + (s - 1) * P

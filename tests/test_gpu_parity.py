@@ -13,7 +13,8 @@ import torch
 import oracle
 import paged_kv_cache_452_amd as pkv
 import workloads
-from helpers import (assert_close, gpu_decode, oracle_decode, poison_dead_slots_, say, words)
+from helpers import (assert_close, gpu_decode, oracle_decode, poison_dead_slots_, say, set_plane_,
+                     words)
 
 pytestmark = pytest.mark.gpu
 
@@ -282,8 +283,8 @@ def _poison_new_slots_(k, v, t, Hkv, D, B):
                 idx.append((oracle.pool_index(False, b, h, (n - 1) % B, d, Hkv, B, D),
                             oracle.pool_index(True, b, h, (n - 1) % B, d, Hkv, B, D)))
     ia = torch.tensor(idx, dtype=torch.long, device=k.device)
-    k.view(-1)[ia[:, 0]] = float("nan")
-    v.view(-1)[ia[:, 1]] = float("nan")
+    set_plane_(k, ia[:, 0], float("nan"))
+    set_plane_(v, ia[:, 1], float("nan"))
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,dtype,lens,B,nwg", [

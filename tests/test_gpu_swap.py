@@ -39,25 +39,22 @@ _CODE = {"bf16": pkv.PKV_BF16, "fp16": pkv.PKV_FP16, "fp8": pkv.PKV_FP8_E4M3}
 
 
 def _pools(L, NB, NBH, Hkv, D, B, kind, seed):
-    """Device pool of NB blocks and pinned host pool of NBH blocks, both filled with different
-    random contents."""
+    """Device pool of NB blocks and pinned host pool of NBH blocks ([L][blocks][Hkv][K, V][tile]),
+    both filled with different random contents."""
     gd = torch.Generator(device=DEV).manual_seed(seed)
     gh = torch.Generator().manual_seed(seed + 1)
-    dk = _fill((L, NB, Hkv, B * D), kind, gd, DEV)
-    dv = _fill((L, NB, Hkv, B * D), kind, gd, DEV)
-    hk = _fill((L, NBH, Hkv, B * D), kind, gh, "cpu").pin_memory()
-    hv = _fill((L, NBH, Hkv, B * D), kind, gh, "cpu").pin_memory()
-    esz = dk.element_size()
-    dpool = pkv.kv_pool_create(dk, dv, dk.numel() * esz, L, NB, Hkv, D, B, _CODE[kind])
-    hpool = pkv.kv_pool_create(hk, hv, hk.numel() * esz, L, NBH, Hkv, D, B, _CODE[kind])
-    return (dk, dv, hk, hv), dpool, hpool
+    dkv = _fill((L, NB, Hkv, 2, B * D), kind, gd, DEV)
+    hkv = _fill((L, NBH, Hkv, 2, B * D), kind, gh, "cpu").pin_memory()
+    esz = dkv.element_size()
+    dpool = pkv.kv_pool_create(dkv, dkv.numel() * esz, L, NB, Hkv, D, B, _CODE[kind])
+    hpool = pkv.kv_pool_create(hkv, hkv.numel() * esz, L, NBH, Hkv, D, B, _CODE[kind])
+    return (dkv, hkv), dpool, hpool
 
 
-def _copy_host(dst_k, dst_v, src_k, src_v, pairs):
-    """Oracle of a whole-block copy on [L][blocks][...] byte arrays."""
+def _copy_host(dst, src, pairs):
+    """Oracle of a whole-block copy on [L][blocks][...] byte arrays (a block's K and V)."""
     for s, d in pairs:
-        dst_k[:, d] = src_k[:, s]
-        dst_v[:, d] = src_v[:, s]
+        dst[:, d] = src[:, s]
 
 
 def _ids(a, where):
@@ -69,61 +66,54 @@ def _ids(a, where):
                                       ("bf16", 128, 32), ("fp8", 64, 32)])
 def test_swap_out_then_in_bit_exact(kind, D, B):
     L, NB, NBH, Hkv = 3, 40, 24, 4
-    (dk, dv, hk, hv), dpool, hpool = _pools(L, NB, NBH, Hkv, D, B, kind, seed=D + B)
+    (dkv, hkv), dpool, hpool = _pools(L, NB, NBH, Hkv, D, B, kind, seed=D + B)
     rng = np.random.default_rng(D * B)
     n = 10
     dev_blocks = rng.permutation(NB)[:n]
     host_blocks = rng.permutation(NBH)[:n]
     out_pairs = list(zip(dev_blocks.tolist(), host_blocks.tolist()))
-    dkb, dvb, hkb, hvb = _raw(dk), _raw(dv), _raw(hk), _raw(hv)
-    sh = (L, -1)
-    want_hk, want_hv = hkb.reshape(L, NBH, -1).copy(), hvb.reshape(L, NBH, -1).copy()
-    _copy_host(want_hk, want_hv, dkb.reshape(L, NB, -1), dvb.reshape(L, NB, -1), out_pairs)
+    dkb = _raw(dkv).reshape(L, NB, -1)
+    want_h = _raw(hkv).reshape(L, NBH, -1).copy()
+    _copy_host(want_h, dkb, out_pairs)
     say("swap out", kind, D, B)
     pkv.swap_blocks(dpool, hpool, _ids(dev_blocks, "device"), _ids(host_blocks, "device"),
                     pkv.PKV_SWAP_OUT)
     torch.cuda.synchronize()
-    assert np.array_equal(_raw(hk).reshape(sh), want_hk.reshape(sh))
-    assert np.array_equal(_raw(hv).reshape(sh), want_hv.reshape(sh))
-    assert np.array_equal(_raw(dk), dkb) and np.array_equal(_raw(dv), dvb)   # source untouched
+    assert np.array_equal(_raw(hkv).reshape(L, NBH, -1), want_h)
+    assert np.array_equal(_raw(dkv).reshape(L, NB, -1), dkb)   # source untouched
 
     # the device blocks are reused (overwritten), then the swapped blocks come back elsewhere
     g = torch.Generator(device=DEV).manual_seed(7)
     idx = torch.from_numpy(dev_blocks).to(DEV)
-    dk[:, idx] = _fill(dk[:, idx].shape, kind, g, DEV)
-    dv[:, idx] = _fill(dv[:, idx].shape, kind, g, DEV)
+    dkv[:, idx] = _fill(tuple(dkv[:, idx].shape), kind, g, DEV)
     back = rng.permutation(NB)[:n]
     in_pairs = list(zip(host_blocks.tolist(), back.tolist()))
-    dkb2, dvb2 = _raw(dk).reshape(L, NB, -1).copy(), _raw(dv).reshape(L, NB, -1).copy()
-    _copy_host(dkb2, dvb2, want_hk, want_hv, in_pairs)
+    dkb2 = _raw(dkv).reshape(L, NB, -1).copy()
+    _copy_host(dkb2, want_h, in_pairs)
     say("swap in", kind, D, B)
     pkv.swap_blocks(dpool, hpool, _ids(host_blocks, "device"), _ids(back, "device"),
                     pkv.PKV_SWAP_IN)
     torch.cuda.synchronize()
-    assert np.array_equal(_raw(dk).reshape(sh), dkb2.reshape(sh))
-    assert np.array_equal(_raw(dv).reshape(sh), dvb2.reshape(sh))
+    assert np.array_equal(_raw(dkv).reshape(L, NB, -1), dkb2)
     # round trip: block back[i] holds what dev_blocks[i] held before the swap out
     for a, b in zip(dev_blocks, back):
-        assert np.array_equal(_raw(dk[:, int(b)]).reshape(L, -1), dkb.reshape(L, NB, -1)[:, a])
-        assert np.array_equal(_raw(dv[:, int(b)]).reshape(L, -1), dvb.reshape(L, NB, -1)[:, a])
+        assert np.array_equal(_raw(dkv[:, int(b)]).reshape(L, -1), dkb[:, a])
     dpool.destroy()
     hpool.destroy()
 
 
 def test_swap_ids_in_pinned_host_memory_and_out_of_range_skipped():
     L, NB, NBH, Hkv, D, B = 2, 16, 12, 2, 128, 16
-    (dk, dv, hk, hv), dpool, hpool = _pools(L, NB, NBH, Hkv, D, B, "bf16", seed=3)
+    (dkv, hkv), dpool, hpool = _pools(L, NB, NBH, Hkv, D, B, "bf16", seed=3)
     src = [3, 7, NB, -1, 0]             # two pairs name a block outside the device pool
     dst = [0, 11, 5, 6, NBH]            # and one outside the host pool
     valid = [(3, 0), (7, 11)]
-    want_hk = _raw(hk).reshape(L, NBH, -1).copy()
-    want_hv = _raw(hv).reshape(L, NBH, -1).copy()
-    _copy_host(want_hk, want_hv, _raw(dk).reshape(L, NB, -1), _raw(dv).reshape(L, NB, -1), valid)
+    want_h = _raw(hkv).reshape(L, NBH, -1).copy()
+    _copy_host(want_h, _raw(dkv).reshape(L, NB, -1), valid)
     say("swap out, ids in pinned host memory")
     pkv.swap_blocks(dpool, hpool, _ids(src, "host"), _ids(dst, "host"), pkv.PKV_SWAP_OUT)
     torch.cuda.synchronize()
-    assert np.array_equal(_raw(hk).reshape(L, NBH, -1), want_hk)
-    assert np.array_equal(_raw(hv).reshape(L, NBH, -1), want_hv)
+    assert np.array_equal(_raw(hkv).reshape(L, NBH, -1), want_h)
     dpool.destroy()
     hpool.destroy()
 
@@ -138,20 +128,17 @@ def _aligned_pageable(shape):
 
 def test_swap_refuses_pageable_host_pool_and_mismatched_geometry():
     L, NB, Hkv, D, B = 1, 8, 2, 64, 16
-    dk = torch.zeros((L, NB, Hkv, B * D), dtype=torch.bfloat16, device=DEV)
-    dv = torch.zeros_like(dk)
-    pk = _aligned_pageable((L, NB, Hkv, B * D))                     # pageable: not pinned
-    pv = _aligned_pageable((L, NB, Hkv, B * D))
-    dpool = pkv.kv_pool_create(dk, dv, dk.numel() * 2, L, NB, Hkv, D, B, pkv.PKV_BF16)
-    ppool = pkv.kv_pool_create(pk, pv, pk.numel() * 2, L, NB, Hkv, D, B, pkv.PKV_BF16)
+    dkv = torch.zeros((L, NB, Hkv, 2, B * D), dtype=torch.bfloat16, device=DEV)
+    pkv_ = _aligned_pageable((L, NB, Hkv, 2, B * D))                # pageable: not pinned
+    dpool = pkv.kv_pool_create(dkv, dkv.numel() * 2, L, NB, Hkv, D, B, pkv.PKV_BF16)
+    ppool = pkv.kv_pool_create(pkv_, pkv_.numel() * 2, L, NB, Hkv, D, B, pkv.PKV_BF16)
     ids = _ids([0, 1], "device")
     say("swap with a pageable host pool (must be refused before any launch)")
     with pytest.raises(pkv.PagedKVError) as e:
         pkv.swap_blocks(dpool, ppool, ids, ids, pkv.PKV_SWAP_OUT)
     assert e.value.status == -1
-    hk = torch.zeros((L, NB, Hkv, B * 128), dtype=torch.bfloat16).pin_memory()
-    hv = torch.zeros_like(hk).pin_memory()
-    hpool = pkv.kv_pool_create(hk, hv, hk.numel() * 2, L, NB, Hkv, 128, B, pkv.PKV_BF16)
+    hkv = torch.zeros((L, NB, Hkv, 2, B * 128), dtype=torch.bfloat16).pin_memory()
+    hpool = pkv.kv_pool_create(hkv, hkv.numel() * 2, L, NB, Hkv, 128, B, pkv.PKV_BF16)
     with pytest.raises(pkv.PagedKVError) as e:
         pkv.swap_blocks(dpool, hpool, ids, ids, pkv.PKV_SWAP_IN)   # head_dim differs
     assert e.value.status == -1
@@ -171,12 +158,11 @@ def test_preempt_reuse_resume_decode():
     dt = torch.bfloat16
     bm = pkv.BlockManager(NB, B, num_host_blocks=NBH)
     g = torch.Generator(device=DEV).manual_seed(21)
-    k = torch.full((1, NB, Hkv, B * D), float("nan"), dtype=dt, device=DEV)
-    v = torch.full((1, NB, Hkv, B * D), float("nan"), dtype=dt, device=DEV)
-    hk = torch.zeros((1, NBH, Hkv, B * D), dtype=dt).pin_memory()
-    hv = torch.zeros_like(hk).pin_memory()
-    dpool = pkv.kv_pool_create(k, v, k.numel() * 2, 1, NB, Hkv, D, B, pkv.PKV_BF16)
-    hpool = pkv.kv_pool_create(hk, hv, hk.numel() * 2, 1, NBH, Hkv, D, B, pkv.PKV_BF16)
+    kv = workloads.new_pool(1, NB, Hkv, B, D, dt, DEV).fill_(float("nan"))
+    k, v = workloads.planes(kv)
+    hkv = workloads.new_pool(1, NBH, Hkv, B, D, dt, "cpu", pin_memory=True).zero_()
+    dpool = pkv.kv_pool_create(kv, kv.numel() * 2, 1, NB, Hkv, D, B, pkv.PKV_BF16)
+    hpool = pkv.kv_pool_create(hkv, hkv.numel() * 2, 1, NBH, Hkv, D, B, pkv.PKV_BF16)
 
     def write_prompt(seq, n):
         bm.allocate(seq, n)

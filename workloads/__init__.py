@@ -190,13 +190,14 @@ class Batch:
     spec: Spec
     tables: Tables
     q: torch.Tensor            # [S][Hq][D]
-    k_pool: torch.Tensor       # [L][NB][Hkv][B*D]
-    v_pool: torch.Tensor
+    k_pool: torch.Tensor       # [L][NB][Hkv][B*D]: the K plane of kv_pool (a strided view)
+    v_pool: torch.Tensor       # the V plane
     new_key: torch.Tensor      # [T][Hkv][D]
     new_value: torch.Tensor
     block_tables: torch.Tensor  # int32, on device
     context_lens: torch.Tensor  # int32, on device
     slot_mapping: torch.Tensor  # int64, on device
+    kv_pool: Optional[torch.Tensor] = None  # [L][NB][Hkv][2][B*D], the one allocation
 
     @property
     def scale(self) -> float:
@@ -211,6 +212,20 @@ def randn(shape, dtype, generator: torch.Generator, device) -> torch.Tensor:
     """N(0,1) drawn in fp32 and rounded to `dtype` (round to nearest even)."""
     return torch.randn(shape, generator=generator, dtype=torch.float32,
                        device=device).to(dtype)
+
+
+def new_pool(num_layers: int, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+             dtype, device, pin_memory: bool = False) -> torch.Tensor:
+    """An uninitialised KV pool in the library's layout: [layer][block][kv_head][K tile, V tile],
+    as a tensor [L][NB][Hkv][2][B*D] (one allocation; see planes)."""
+    return torch.empty((num_layers, num_blocks, num_kv_heads, 2, block_size * head_dim),
+                       dtype=dtype, device=device, pin_memory=pin_memory)
+
+
+def planes(pool: torch.Tensor):
+    """The K and V planes of a pool from new_pool: views [L][NB][Hkv][B*D] whose layer slices
+    have the addresses kv_pool_layer gives."""
+    return pool.select(-2, 0), pool.select(-2, 1)
 
 
 def fill_pool_(pool: torch.Tensor, generator: torch.Generator, chunk_elems: int = 1 << 28):
@@ -257,8 +272,8 @@ def make_batch_fp8(spec: Spec, device="cpu", tables: Optional[Tables] = None,
     g.manual_seed((spec.seed if seed is None else seed) * 7919 + 23)
     dt = spec.torch_dtype
     q = randn((S, Hq, D), dt, g, device)
-    k_pool = fill_pool_fp8_(torch.empty((L, NB, Hkv, B * D), dtype=torch.uint8, device=device), g)
-    v_pool = fill_pool_fp8_(torch.empty((L, NB, Hkv, B * D), dtype=torch.uint8, device=device), g)
+    kv = fill_pool_fp8_(new_pool(L, NB, Hkv, B, D, torch.uint8, device), g)
+    k_pool, v_pool = planes(kv)
     if not tables.used_blocks.all():
         unused = torch.from_numpy(np.nonzero(~tables.used_blocks)[0]).to(device)
         k_pool[:, unused] = E4M3_NAN
@@ -269,7 +284,7 @@ def make_batch_fp8(spec: Spec, device="cpu", tables: Optional[Tables] = None,
     return Batch(spec, tables, q, k_pool, v_pool, new_key, new_value,
                  torch.from_numpy(tables.block_tables).to(device),
                  torch.from_numpy(tables.context_lens).to(device),
-                 torch.from_numpy(tables.slot_mapping).to(device))
+                 torch.from_numpy(tables.slot_mapping).to(device), kv)
 
 
 def make_batch(spec: Spec, device="cpu", tables: Optional[Tables] = None,
@@ -285,10 +300,8 @@ def make_batch(spec: Spec, device="cpu", tables: Optional[Tables] = None,
     g.manual_seed((spec.seed if seed is None else seed) * 7919 + 17)
     dt = spec.torch_dtype
     q = randn((S, Hq, D), dt, g, device)
-    k_pool = torch.empty((L, NB, Hkv, B * D), dtype=dt, device=device)
-    v_pool = torch.empty((L, NB, Hkv, B * D), dtype=dt, device=device)
-    fill_pool_(k_pool, g)
-    fill_pool_(v_pool, g)
+    kv = fill_pool_(new_pool(L, NB, Hkv, B, D, dt, device), g)
+    k_pool, v_pool = planes(kv)
     if poison_unused and not tables.used_blocks.all():
         unused = torch.from_numpy(np.nonzero(~tables.used_blocks)[0]).to(device)
         k_pool[:, unused] = float("nan")
@@ -299,4 +312,4 @@ def make_batch(spec: Spec, device="cpu", tables: Optional[Tables] = None,
     return Batch(spec, tables, q, k_pool, v_pool, new_key, new_value,
                  torch.from_numpy(tables.block_tables).to(device),
                  torch.from_numpy(tables.context_lens).to(device),
-                 torch.from_numpy(tables.slot_mapping).to(device))
+                 torch.from_numpy(tables.slot_mapping).to(device), kv)
