@@ -43,6 +43,25 @@ def algorithmic_bytes(lens, num_q_heads, num_kv_heads, head_dim, elem=2, block=1
     return kv + qo + tables + 4 * len(lens)
 
 
+def unique_kv_bytes(block_tables, lens, num_kv_heads, head_dim, kv_elem=2, block=16):
+    """K and V bytes of one launch counting each physical block once: for every block some table
+    references, the slots any sequence uses in it (a shared prefix block is read by every
+    sequence that shares it, but holds its bytes once)."""
+    used = {}
+    for s, n in enumerate(lens):
+        n = int(n)
+        for j in range(-(-n // block)):
+            b = int(block_tables[s][j])
+            used[b] = max(used.get(b, 0), min(block, n - j * block))
+    return sum(used.values()) * num_kv_heads * head_dim * kv_elem * 2
+
+
+def percentiles(xs, qs=(10, 50, 90)):
+    """Nearest-rank percentiles of a small list."""
+    xs = sorted(xs)
+    return {f"p{q}": xs[min(len(xs) - 1, max(0, -(-q * len(xs) // 100) - 1))] for q in qs}
+
+
 def code_hash(text: str) -> str:
     """Hash of a C++ source with its // comments, trailing spaces and blank lines removed, so that
     a comment edit does not invalidate counters taken on the same code."""
@@ -402,9 +421,18 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     # Timed region B: the decode kernel alone, launched back to back over the layers; the mean
-    # launch duration is the region's time over the launch count.
+    # launch duration is the region's time over the launch count. An event after every sweep
+    # (between launches, not inside any) also gives the spread of the per-sweep means.
     reps_b = max(1, args.steps // 2)
-    avg_decode_ms = timed(sweep_decode, reps_b) / (reps_b * L)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps_b + 1)]
+    torch.cuda.synchronize()
+    marks[0].record(stream)
+    for r in range(reps_b):
+        sweep_decode()
+        marks[r + 1].record(stream)
+    torch.cuda.synchronize()
+    avg_decode_ms = marks[0].elapsed_time(marks[-1]) / (reps_b * L)
+    sweep_us = [marks[r].elapsed_time(marks[r + 1]) * 1e3 / L for r in range(reps_b)]
     # Timed region A: whole steps (per layer: reshape_and_cache, then decode), no markers inside.
     ms_total = timed(step, args.steps)
     ms_step = ms_total / args.steps
@@ -444,6 +472,8 @@ def main() -> int:
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_per_layer_step": round(S * L / (ms_step * 1e-3), 1),
         "decode_launch_us": round(avg_decode_ms * 1e3, 2),
+        "decode_launch_us_spread": dict({k: round(v, 2) for k, v in percentiles(sweep_us).items()},
+                                        sweeps=reps_b, launches_per_sweep=L),
         "timing": "roofline.achieved: back-to-back step launches of the decode kernel over all "
                   "layers between two HIP events on the launch stream (mean launch duration), "
                   "timed first; value: K whole steps between two HIP events",
@@ -455,6 +485,19 @@ def main() -> int:
                                 "paged_attention_decode_append") +
                                " (one persistent decode kernel; split streams merged in it)"},
     }
+    uniq = unique_kv_bytes(t.block_tables, t.context_lens, Hkv, D, kv_elem=1 if fp8 else 2,
+                           block=B)
+    logical = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=1 if fp8 else 2) - \
+        algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=0)
+    if uniq < logical:   # blocks shared between sequences (a common prefix)
+        rec["unique_kv"] = {"bytes_per_launch": uniq, "logical_kv_bytes_per_launch": logical,
+                            "gbps_at_decode_time": round(uniq / (avg_decode_ms * 1e-3) / 1e9, 2),
+                            "what": "K/V bytes counting each physical block once (a shared "
+                                    "prefix is read by every sharer but stored once)"}
+    props = torch.cuda.get_device_properties(0)
+    rec["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "compute_units": props.multi_processor_count, "hip": torch.version.hip,
+                     "torch": torch.__version__}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(batch, spec, range(L), kv_scales=(ks, vs) if fp8
                                            else None)

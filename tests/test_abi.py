@@ -164,6 +164,30 @@ def test_binding_refuses_host_tensors():
                                    torch.zeros(1, dtype=torch.int32), 0.125, 4, 4, 64, 16, 0)
 
 
+@pytest.mark.parametrize("dtype,elem", [(pkv.PKV_BF16, 2), (pkv.PKV_FP8_E4M3, 1)])
+@pytest.mark.parametrize("B", [16, 32])
+def test_pool_views_match_kv_pool_layer(dtype, elem, B):
+    """The K and V plane views the tests and the benchmark pass (workloads.new_pool / planes) sit
+    at exactly the addresses kv_pool_layer gives for the same allocation (host memory; nothing is
+    dereferenced), and each plane has the two-tile stride per (block, kv head)."""
+    import torch
+    import workloads
+    L, NB, Hkv, D = 3, 5, 2, 64
+    kv = workloads.new_pool(L, NB, Hkv, B, D, torch.uint8 if elem == 1 else torch.bfloat16, "cpu")
+    nbytes = kv.numel() * kv.element_size()
+    assert nbytes == pkv.kv_pool_bytes(L, NB, Hkv, D, B, dtype)
+    base = kv.data_ptr()
+    k, v = workloads.planes(kv)
+    shift = -base % 256   # kv_pool_create wants a 256-byte aligned base: compare offsets from it
+    pool = pkv.kv_pool_create(base + shift, nbytes, L, NB, Hkv, D, B, dtype)
+    for layer in range(L):
+        kl, vl = pool.layer(layer)
+        assert kl - shift == k[layer].data_ptr() and vl - shift == v[layer].data_ptr()
+        assert vl - kl == B * D * elem                         # V tile right after the K tile
+    assert k.stride(2) == 2 * B * D and k.stride(1) == Hkv * 2 * B * D   # elements
+    pool.destroy()
+
+
 def test_copy_blocks_argument_errors():
     lib = pkv.load_library()
     total = pkv.kv_pool_bytes(2, 16, 4, 128, 16, pkv.PKV_BF16)

@@ -32,3 +32,24 @@ def test_code_hash_ignores_comments_only():
     c = "int f(int x) {\n  return 3 * x;\n}\n"
     assert bench.code_hash(a) == bench.code_hash(b)
     assert bench.code_hash(a) != bench.code_hash(c)
+
+
+def test_unique_kv_bytes_counts_shared_blocks_once():
+    # Two sequences share physical blocks 5 and 9 (a 32-token prefix); sequence 0 then has 3
+    # tokens in block 2, sequence 1 has 20 tokens in blocks 7 (full) and 4 (4 tokens).
+    tables = np.array([[5, 9, 2, -1], [5, 9, 7, 4]], np.int32)
+    lens = np.array([35, 52])
+    row = 2 * 64 * 2 * 2     # one token: 2 kv heads x 64 dims x 2 B, K and V
+    assert bench.unique_kv_bytes(tables, lens, 2, 64) == (16 + 16 + 3 + 16 + 4) * row
+    # no sharing: the same as the logical K/V bytes
+    private = np.array([[0, 1, -1, -1], [2, 3, 4, 5]], np.int32)
+    assert bench.unique_kv_bytes(private, lens, 2, 64) == int(lens.sum()) * row
+    # fp8 pools hold one byte per element
+    assert bench.unique_kv_bytes(tables, lens, 2, 64, kv_elem=1) * 2 == \
+        bench.unique_kv_bytes(tables, lens, 2, 64)
+
+
+def test_percentiles_nearest_rank():
+    assert bench.percentiles([5, 1, 4, 2, 3]) == {"p10": 1, "p50": 3, "p90": 5}
+    assert bench.percentiles(list(range(1, 11))) == {"p10": 1, "p50": 5, "p90": 9}
+    assert bench.percentiles([7.0]) == {"p10": 7.0, "p50": 7.0, "p90": 7.0}
