@@ -319,9 +319,13 @@ paged_decode_kernel(DecodeLaunch a) {
     cur = stream_at(s0, (r0 - Hh * pb) / nb);
   }
 
-  // ---- q: the head rows of the range's first streams, staged in LDS for all four waves. ----
+  // ---- q: the head rows of the range's first streams, staged in LDS for all four waves. The
+  // loads go out here; the rows are stored into LDS after the tile-id loads below have gone out
+  // too, so that the start-up waits for one memory round trip instead of three. ----
   int staged_left;  // staged streams after the current one
   int next_qrow;    // LDS row of the next staged stream
+  int q_rows;       // staged rows
+  u32x4 qbuf[kQLoads];
   {
     int rows = 0, nstaged = 0;
     Stream t = cur;
@@ -333,31 +337,33 @@ paged_decode_kernel(DecodeLaunch a) {
       t = stream_after(t);
     }
     __syncthreads();
-    u32x4 buf[kQLoads];
+    // Unconditional loads (rows past the staged ones reread row 0 and are not stored): no branch
+    // around them, so nothing waits for them before the tile-id loads go out.
 #pragma unroll
     for (int u = 0; u < kQLoads; ++u) {
       const int c = tid + kThreads * u;
-      const int row = c / kChunks;
-      buf[u] = row < rows
-                   ? load16((const char*)a.q + ((size_t)s_scan[row] * D + (c % kChunks) * 8) * 2)
-                   : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kQLoads; ++u) {
-      const int c = tid + kThreads * u;
-      if (c / kChunks < rows) s_q[c / kChunks][c % kChunks] = buf[u];
+      const int row = c / kChunks < rows ? c / kChunks : 0;
+      qbuf[u] = load16((const char*)a.q + ((size_t)s_scan[row] * D + (c % kChunks) * 8) * 2);
     }
     staged_left = nstaged - 1;
     next_qrow = cur.nvalid;
+    q_rows = rows;
   }
 
   // ---- Tile ids: lane l of window c holds the 16-token sub-tile of this wave's position 64c + l
   // (its index in units of 16 * D elements of the layer's K or V plane). ----
   const int span = r1 - r0;
   const int mw = span > wave ? (span - wave + kWaves - 1) / kWaves : 0;  // this wave's blocks
-  auto window = [&](int c) -> unsigned {
+  // The block id of lane l's position in window c, and what the tile index adds to
+  // (block id * num_kv_heads) << (sub_shift + 1): the load is issued here and used later, so
+  // that several windows' loads can be in flight together.
+  struct Win {
+    unsigned b;    // block_tables entry (0 past the range)
+    unsigned add;  // (kv head << (sub_shift + 1)) + sub-tile
+  };
+  auto window_load = [&](int c) -> Win {
     const int p = r0 + wave + kWaves * (64 * c + lane);
-    if (p >= r1) return 0u;
+    if (p >= r1) return Win{0u, 0u};
     const int s = seq_of(p);
     const int pb = s_ps[s];
     const int nb = s_ps[s + 1] - pb;
@@ -369,12 +375,25 @@ paged_decode_kernel(DecodeLaunch a) {
     // (R = block_size / 16 sub-tiles per block, each 16 * D elements of the block's tile). Tiles
     // of one plane lie two apart (the K and V tiles of a (block, head) alternate), so the K and V
     // sub-tile both sit at this index times 16 * D elements from their plane's base.
-    const unsigned b = (unsigned)a.block_tables[(size_t)s * a.max_blocks + (j >> a.sub_shift)];
-    return ((b * (unsigned)a.num_kv_heads + (unsigned)g) << (a.sub_shift + 1)) +
-           (unsigned)(j & ((1 << a.sub_shift) - 1));
+    return Win{(unsigned)a.block_tables[(size_t)s * a.max_blocks + (j >> a.sub_shift)],
+               ((unsigned)g << (a.sub_shift + 1)) + (unsigned)(j & ((1 << a.sub_shift) - 1))};
   };
-  unsigned win_a = window(0);
-  unsigned win_b = mw > 64 ? window(1) : 0u;
+  auto tile_index = [&](const Win& w) -> unsigned {
+    return ((w.b * (unsigned)a.num_kv_heads) << (a.sub_shift + 1)) + w.add;
+  };
+  auto window = [&](int c) -> unsigned { return tile_index(window_load(c)); };
+  unsigned win_a, win_b;
+  {
+    const Win w0 = window_load(0);
+    const Win w1 = mw > 64 ? window_load(1) : Win{0u, 0u};
+#pragma unroll
+    for (int u = 0; u < kQLoads; ++u) {
+      const int c = tid + kThreads * u;
+      if (c / kChunks < q_rows) s_q[c / kChunks][c % kChunks] = qbuf[u];
+    }
+    win_a = tile_index(w0);
+    win_b = tile_index(w1);
+  }
   if constexpr (APPEND) {
     // The step's new token of every stream whose last unit lies in this range goes into the pool
     // here, before any tile is read: the workgroup that reads that unit writes it itself (head
