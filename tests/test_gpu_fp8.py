@@ -176,17 +176,17 @@ def test_fp8_step_reshape_then_decode():
     assert rel <= 2e-3, rel
 
 
-def test_fp8_config4_80_layers_sampled():
+def test_fp8_70b_shaped_80_layers_sampled():
     """70B-shaped over fp8 pools, 80 layers decoded as the benchmark does; sampled (sequence,
     head) outputs of sampled layers against the oracle."""
     spec = workloads.SPECS[4]
     t = workloads.make_tables(spec)
-    say("fp8 config 4: allocating and filling 2 x 20 GiB")
+    say("fp8 pools, 70B-shaped batch: allocating and filling 2 x 20 GiB")
     b = workloads.make_batch_fp8(spec, device=DEV, tables=t)
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     outs = torch.empty((spec.num_layers, S, Hq, D), dtype=b.q.dtype, device=DEV)
     ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, 4096), DEV)
-    say("fp8 config 4: decode 80 layers")
+    say("fp8 pools, 70B-shaped batch: decode 80 layers")
     for L in range(spec.num_layers):
         pkv.paged_attention_decode_fp8(outs[L], b.q, b.k_pool[L], b.v_pool[L], b.block_tables,
                                        b.context_lens, spec.scale, 0.5, 0.5, Hq, Hkv, D, 16,

@@ -77,7 +77,7 @@ def test_shared_prefix_equals_private_copies():
     assert torch.equal(shared.view(torch.int16), private.view(torch.int16))
     ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, spec.num_q_heads,
                         spec.num_kv_heads, t.num_blocks)
-    assert_close(shared, ref, "config 5")
+    assert_close(shared, ref, "shared-prefix batch")
 
 
 def test_dead_slots_and_table_padding_are_never_read():

@@ -66,7 +66,7 @@ def test_decode_step_matches_oracle(idx):
     assert_close(out, ref, spec.name)
 
 
-def test_config1_two_steps_cross_block_boundary():
+def test_tiny_batch_two_steps_cross_block_boundary():
     spec = workloads.SPECS[1]
     batch = workloads.make_batch(spec, device=DEV)
     out, ref = _step(batch)
@@ -86,17 +86,17 @@ def test_config1_two_steps_cross_block_boundary():
     assert_close(out2, ref2, "step 2")
 
 
-def test_config4_all_80_layers_sampled():
+def test_70b_shaped_all_80_layers_sampled():
     """70B-shaped: 80 layers in one 80 GiB pool, decoded layer by layer as the benchmark does;
     sampled (sequence, head) outputs of sampled layers against the oracle."""
     spec = workloads.SPECS[4]
     t = workloads.make_tables(spec)
-    say("config 4: allocating and filling 2 x 40 GiB")
+    say("70B-shaped batch: allocating and filling 2 x 40 GiB")
     batch = workloads.make_batch(spec, device=DEV, tables=t)
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     outs = torch.empty((spec.num_layers, S, Hq, D), dtype=batch.q.dtype, device=DEV)
     ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, 4096), DEV)
-    say("config 4: decode 80 layers")
+    say("70B-shaped batch: decode 80 layers")
     for L in range(spec.num_layers):
         k, v = _layer(batch, L)
         pkv.paged_attention_decode(outs[L], batch.q, k, v, batch.block_tables, batch.context_lens,
@@ -325,12 +325,12 @@ def test_fused_append_decode_matches_oracle(Hq, Hkv, D, dtype, lens, B, nwg):
             assert torch.equal(out[s].view(torch.int16), b.new_value[s][g].view(torch.int16))
 
 
-def test_fused_append_config4_80_layers_sampled():
+def test_fused_append_70b_shaped_80_layers_sampled():
     """The benchmark's fused step on the 70B-shaped batch: every layer appends and decodes in one
     launch; sampled outputs of sampled layers and the written slots against the oracle."""
     spec = workloads.SPECS[4]
     t = workloads.make_tables(spec)
-    say("fused config 4: allocating and filling 2 x 40 GiB")
+    say("fused step, 70B-shaped batch: allocating and filling 2 x 40 GiB")
     batch = workloads.make_batch(spec, device=DEV, tables=t)
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     outs = torch.empty((spec.num_layers, S, Hq, D), dtype=batch.q.dtype, device=DEV)
@@ -341,7 +341,7 @@ def test_fused_append_config4_80_layers_sampled():
         oracle.reshape_and_cache(kw, vw, batch.new_key.cpu(), batch.new_value.cpu(),
                                  t.slot_mapping, Hkv, D, 16, t.num_blocks)
         want[L] = (kw, vw)
-    say("fused config 4: 80 layers")
+    say("fused step, 70B-shaped batch: 80 layers")
     for L in range(spec.num_layers):
         pkv.paged_attention_decode_append(outs[L], batch.q, batch.new_key, batch.new_value,
                                           batch.k_pool[L], batch.v_pool[L], batch.block_tables,

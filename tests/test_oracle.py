@@ -198,7 +198,7 @@ def test_oracle_matches_torch_sdpa(Hq, Hkv, D, dtype, lens):
 
 
 def test_oracle_matches_bruteforce_loop():
-    """Config-1 shape checked by a direct triple loop in Python floats."""
+    """The tiny 4-sequence shape checked by a direct triple loop in Python floats."""
     Hq = Hkv = 4
     D, B = 64, 16
     lens = [1, 15, 16, 41]

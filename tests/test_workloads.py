@@ -45,7 +45,7 @@ def test_tables_are_valid_block_maps(idx):
     assert np.array_equal(used, t.used_blocks)
 
 
-def test_config_shapes():
+def test_workload_shapes():
     t1 = make_tables(SPECS[1])
     assert t1.context_lens.tolist() == [1, 15, 16, 41] and t1.num_blocks == 64
     t2 = make_tables(SPECS[2])

@@ -1,7 +1,7 @@
 """Seeded synthetic decode batches (shared input source for tests, smoke check and benchmark).
 
 This module draws random numbers and builds host-side block tables; it performs none of the
-attention or scatter arithmetic. Everything is seeded, so a (config, seed) pair names one input.
+attention or scatter arithmetic. Everything is seeded, so a (workload, seed) pair names one input.
 
 Shapes follow the five decode workloads this library is measured on:
   1. tiny MHA       S=4, context {1,15,16,41}, 4/4 heads, d64, bf16, pool of 64 blocks
@@ -74,7 +74,7 @@ class Tables:
     num_blocks: int                 # physical blocks per layer in the pool
     slot_mapping: np.ndarray        # int64 [T], the step's new tokens
     used_blocks: np.ndarray         # bool [num_blocks], referenced by some table
-    shared_prefix_blocks: int = 0   # config 5: leading table entries shared by the first 50 seqs
+    shared_prefix_blocks: int = 0   # shared-prefix batch: leading table entries shared by its first 50 seqs
     free_list: Optional[List[int]] = None  # remaining free blocks, front first
 
 
@@ -115,7 +115,7 @@ def _lens(spec: Spec, rng: np.random.Generator) -> np.ndarray:
 
 def make_tables(spec: Spec, lens: Optional[np.ndarray] = None, pool_factor: float = 1.5,
                 num_blocks: Optional[int] = None, seed: Optional[int] = None) -> Tables:
-    """Block tables, context lengths and the step's slot mapping for a config (seeded)."""
+    """Block tables, context lengths and the step's slot mapping for a workload (seeded)."""
     rng = np.random.default_rng(spec.seed if seed is None else seed)
     B = spec.block_size
     if lens is None:
