@@ -203,31 +203,45 @@ paged_decode_kernel(DecodeLaunch a) {
   const int S = a.num_seqs;
 
   // ---- Plan: block counts per sequence and their prefix sum, in LDS. ----
+  bool same_len;  // every sequence has as many units as sequence 0
   {
     const int chunk = (S + kThreads - 1) / kThreads;
     const int lo = min(S, tid * chunk);
     const int hi = min(S, lo + chunk);
+    const int nb0 = (min(max(a.context_lens[0], 0), a.max_tokens) + kBlock - 1) / kBlock;
     int sum = 0;
+    bool same = true;
     for (int i = lo; i < hi; ++i) {
       const int n = min(max(a.context_lens[i], 0), a.max_tokens);
       s_len[i] = n;
-      sum += (n + kBlock - 1) / kBlock;
+      const int nb = (n + kBlock - 1) / kBlock;
+      sum += nb;
+      same = same && nb == nb0;
     }
-    s_scan[tid] = sum;
+    // Exclusive prefix sum of the per-thread sums: inside each wavefront by shuffles, then over
+    // the wavefronts' totals (one barrier instead of two per doubling step).
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) s_scan[wave] = incl;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int v = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
+    int base = incl - sum;
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int t = s_scan[w];
+      base += w < wave ? t : 0;
+      total += t;
     }
-    int base = s_scan[tid] - sum;
     for (int i = lo; i < hi; ++i) {
       s_ps[i] = base;
       base += (s_len[i] + kBlock - 1) / kBlock;
     }
-    if (tid == kThreads - 1) s_ps[S] = s_scan[kThreads - 1];
-    __syncthreads();
+    if (tid == 0) s_ps[S] = total;
+    same_len = __syncthreads_and(same);
   }
 
   // Empty sequences (n == 0) own no positions; their output is zero.
@@ -250,12 +264,10 @@ paged_decode_kernel(DecodeLaunch a) {
   //    with W / nwg a whole number of streams): then it splits no stream, and any weighting
   //    would add a merge to every workgroup. Every workgroup sees the same plan, so all decide
   //    alike.
-  bool aligned = W % nwg == 0;
+  bool aligned = same_len && W % nwg == 0;
   if (aligned) {
-    const int L = s_ps[1] - s_ps[0];  // units of the first sequence
+    const int L = s_ps[1] - s_ps[0];  // units of every sequence
     aligned = L > 0 && (W / nwg) % L == 0;
-    for (int i = tid; aligned && i < S; i += kThreads) aligned = s_ps[i + 1] - s_ps[i] == L;
-    aligned = __syncthreads_and(aligned);
   }
   const int odd_w = W >= 2 * nwg && !aligned ? a.odd_weight : kEvenWeight;
   const int r0 = range_start(wg, nwg, W, odd_w);
