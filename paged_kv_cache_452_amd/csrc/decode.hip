@@ -537,10 +537,13 @@ paged_decode_kernel(DecodeLaunch a) {
   // behind another L2.
   auto store_partial = [&](int slot, float M, float L, const float* acc) {
     const size_t pidx = ((size_t)wg * 2 + slot) * kMaxGroupTile + head;
-    float* po = a.ws_o + pidx * D + d0;
+    // Element i of lane l (of the head's lanes) at i * kLanesPerHead + l: each store instruction
+    // writes whole 64-byte runs of the row.
+    float* po = a.ws_o + pidx * D + (lane % kLanesPerHead);
 #pragma unroll
     for (int i = 0; i < kDims; ++i)
-      __hip_atomic_store(po + i, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(po + i * kLanesPerHead, acc[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     if (lane % kLanesPerHead == 0) {
       __hip_atomic_store(a.ws_ml + pidx * 2, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.ws_ml + pidx * 2 + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -645,24 +648,21 @@ paged_decode_kernel(DecodeLaunch a) {
     for (int i = 0; i < kDims; ++i) acc[i] = 0.f;
     for (int k0 = 0; k0 < np; k0 += kMergeRound) {  // parts in a fixed order
       float mp[kMergeRound], lp[kMergeRound];
-      unsigned long long ov[kMergeRound][kDims / 2];
+      float ov[kMergeRound][kDims];
 #pragma unroll
       for (int u = 0; u < kMergeRound; ++u) {
         const size_t pi = part_idx(min(k0 + u, np - 1));  // past the end: reread, weight 0
         mp[u] = ld(a.ws_ml + pi * 2);
         lp[u] = ld(a.ws_ml + pi * 2 + 1);
-        const unsigned long long* po = (const unsigned long long*)(a.ws_o + pi * D + d0);
+        const float* po = a.ws_o + pi * D + (lane % kLanesPerHead);
 #pragma unroll
-        for (int i = 0; i < kDims / 2; ++i)
-          ov[u][i] = __hip_atomic_load(po + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < kDims; ++i) ov[u][i] = ld(po + i * kLanesPerHead);
       }
       if (own && k0 == 0) {  // the same fp32 values the partial would have held
         mp[0] = own_m;
         lp[0] = own_l;
 #pragma unroll
-        for (int i = 0; i < kDims / 2; ++i)
-          ov[0][i] = (unsigned long long)__float_as_uint(own_acc[2 * i]) |
-                     (unsigned long long)__float_as_uint(own_acc[2 * i + 1]) << 32;
+        for (int i = 0; i < kDims; ++i) ov[0][i] = own_acc[i];
       }
       float Mr = M;
 #pragma unroll
@@ -679,10 +679,7 @@ paged_decode_kernel(DecodeLaunch a) {
                                                              : 0.f;
         L += c * lp[u];
 #pragma unroll
-        for (int i = 0; i < kDims / 2; ++i) {
-          acc[2 * i] += c * __uint_as_float((unsigned)ov[u][i]);
-          acc[2 * i + 1] += c * __uint_as_float((unsigned)(ov[u][i] >> 32));
-        }
+        for (int i = 0; i < kDims; ++i) acc[i] += c * ov[u][i];
       }
       M = Mr;
     }
