@@ -2,13 +2,18 @@
 per kv head), head dims, block sizes, element types, context-length mixes with empty, short and
 long sequences, and workgroup counts from 1 to many more than the chip holds. Each case is
 checked against the fp64 oracle to the same bar as the fixed cases (max-abs 1e-2, relative L2
-2e-3), with NaN in every unused block and dead slot."""
+2e-3), with NaN in every unused block and dead slot. The same draws also run over fp8 (E4M3)
+pools with random per-pool scales, and through the fused append step (whose pools must equal the
+oracle's scatter, word for word)."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
+import paged_kv_cache_452_amd as pkv
 import workloads
-from helpers import assert_close, gpu_decode, oracle_decode, poison_dead_slots_, say
+from helpers import (assert_close, gpu_decode, gpu_decode8, oracle_decode, oracle_decode8,
+                     poison_dead_slots_, poison_dead_slots8_, say, set_plane_, words)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,3 +71,81 @@ def test_random_shape_matches_oracle(seed):
     for s, n in enumerate(lens):
         if n == 0:
             assert torch.count_nonzero(out[s]).item() == 0
+
+
+def _spec(tag, seed, Hq, Hkv, D, B, dtype, lens, nwg):
+    return workloads.Spec(0, f"{tag} {seed}: Hq={Hq} Hkv={Hkv} D={D} B={B} {dtype} S={len(lens)} "
+                             f"workgroups={nwg}", len(lens), Hq, Hkv, D,
+                          "bf16" if dtype == torch.bfloat16 else "fp16", 1, seed=seed,
+                          block_size=B)
+
+
+@pytest.mark.parametrize("seed", range(100, 108))
+def test_random_shape_fp8_matches_oracle(seed):
+    Hq, Hkv, D, B, dtype, lens, nwg = random_shape(seed)
+    lens = np.asarray(lens, np.int32)
+    rng = np.random.default_rng(seed)
+    # |V| <= 3.75 * v_scale: v_scale <= 1 keeps |out| below 4, where one bf16 rounding step of
+    # the output (2^-6 on [4, 8)) would already exceed the max-abs bar.
+    k_scale, v_scale = float(2.0 ** rng.integers(-3, 2)), float(rng.uniform(0.05, 1.0))
+    spec = _spec("random fp8", seed, Hq, Hkv, D, B, dtype, lens, nwg)
+    need = sum(-(-int(n) // B) for n in lens)
+    t = workloads.make_tables(spec, lens=lens, num_blocks=need + 5, seed=seed)
+    b = workloads.make_batch_fp8(spec, device=DEV, tables=t)
+    k, v = b.k_pool[0], b.v_pool[0]
+    poison_dead_slots8_(k, v, t.block_tables, t.context_lens, Hkv, D, B)
+    max_ctx = max(int(lens.max()), 1)
+    say("random shape fp8", spec.name, "scales", k_scale, v_scale)
+    out = gpu_decode8(b.q, k, v, b.block_tables, b.context_lens, spec.scale, k_scale, v_scale,
+                      Hq, Hkv, max_ctx, nwg, block_size=B)
+    torch.cuda.synchronize()
+    ref = oracle_decode8(b.q, k, v, t.block_tables, t.context_lens, spec.scale, k_scale, v_scale,
+                         Hq, Hkv, t.num_blocks, block_size=B)
+    assert_close(out, ref, spec.name)
+
+
+def _poison_new_slots_(k, v, t, Hkv, D, B):
+    """NaN into the slot each sequence's new token goes to (the fused step must write it first)."""
+    idx = []
+    for s, n in enumerate(t.context_lens):
+        n = int(n)
+        if n == 0:
+            continue
+        blk = int(t.block_tables[s][(n - 1) // B])
+        for h in range(Hkv):
+            for d in range(D):
+                idx.append((oracle.pool_index(False, blk, h, (n - 1) % B, d, Hkv, B, D),
+                            oracle.pool_index(True, blk, h, (n - 1) % B, d, Hkv, B, D)))
+    if idx:
+        ia = torch.tensor(idx, dtype=torch.long, device=k.device)
+        set_plane_(k, ia[:, 0], float("nan"))
+        set_plane_(v, ia[:, 1], float("nan"))
+
+
+@pytest.mark.parametrize("seed", range(200, 208))
+def test_random_shape_fused_append_matches_oracle(seed):
+    Hq, Hkv, D, B, dtype, lens, nwg = random_shape(seed)
+    lens = np.asarray(lens, np.int32)
+    spec = _spec("random fused", seed, Hq, Hkv, D, B, dtype, lens, nwg)
+    need = sum(-(-int(n) // B) for n in lens)
+    t = workloads.make_tables(spec, lens=lens, num_blocks=need + 5, seed=seed)
+    b = workloads.make_batch(spec, device=DEV, tables=t)
+    k, v = b.k_pool[0], b.v_pool[0]
+    poison_dead_slots_(k, v, t.block_tables, t.context_lens, Hkv, D, B)
+    _poison_new_slots_(k, v, t, Hkv, D, B)
+    kw, vw = words(k), words(v)
+    oracle.reshape_and_cache(kw, vw, b.new_key.cpu(), b.new_value.cpu(), t.slot_mapping, Hkv, D,
+                             B, t.num_blocks)
+    ref = oracle_decode(b.q, None, None, t.block_tables, t.context_lens, spec.scale, Hq, Hkv,
+                        t.num_blocks, k_words=kw, v_words=vw, block_size=B)
+    max_ctx = max(int(lens.max()), 1)
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(len(lens), Hq, Hkv, D, B, max_ctx,
+                                                               nwg), DEV)
+    out = torch.empty_like(b.q)
+    say("random shape fused append", spec.name)
+    pkv.paged_attention_decode_append(out, b.q, b.new_key, b.new_value, k, v, b.block_tables,
+                                      b.context_lens, spec.scale, Hq, Hkv, D, B, max_ctx, nwg, ws)
+    torch.cuda.synchronize()
+    assert_close(out, ref, spec.name)
+    assert np.array_equal(words(k), kw), "K pool differs from the oracle's scatter"
+    assert np.array_equal(words(v), vw), "V pool differs from the oracle's scatter"
