@@ -13,7 +13,7 @@ import oracle
 import paged_kv_cache_452_amd as pkv
 import workloads
 from helpers import (assert_close, gpu_decode, gpu_decode8, oracle_decode, oracle_decode8,
-                     poison_dead_slots_, poison_dead_slots8_, say, set_plane_, words)
+                     codes, poison_dead_slots_, poison_dead_slots8_, say, set_plane_, words)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,3 +149,56 @@ def test_random_shape_fused_append_matches_oracle(seed):
     assert_close(out, ref, spec.name)
     assert np.array_equal(words(k), kw), "K pool differs from the oracle's scatter"
     assert np.array_equal(words(v), vw), "V pool differs from the oracle's scatter"
+
+
+def _scatter_case(seed):
+    """A pool and a multi-token scatter: whole blocks written token by token (as a prompt fills
+    them), scattered single slots, skipped (-1) entries, all in a shuffled order."""
+    rng = np.random.default_rng(5000 + seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.choice([16, 32]))
+    dtype = torch.bfloat16 if rng.random() < 0.5 else torch.float16
+    NB = int(rng.integers(8, 64))
+    blocks = rng.permutation(NB)
+    full = blocks[: int(rng.integers(1, max(2, NB // 4)))]
+    slots = [int(b) * B + t for b in full for t in range(B)]
+    rest = np.setdiff1d(np.arange(NB * B), np.array(slots))
+    slots += [int(x) for x in rng.choice(rest, size=int(rng.integers(1, 60)), replace=False)]
+    slots += [-1] * int(rng.integers(0, 4))
+    slots = np.array(slots, np.int64)[rng.permutation(len(slots))]
+    return Hkv, D, B, dtype, NB, slots
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("fp8", [False, True])
+def test_random_multi_token_scatter_bit_exact(seed, fp8):
+    Hkv, D, B, dtype, NB, slots = _scatter_case(seed)
+    T = len(slots)
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    key = workloads.randn((T, Hkv, D), dtype, gen, DEV)
+    value = workloads.randn((T, Hkv, D), dtype, gen, DEV)
+    sm = torch.from_numpy(slots).to(DEV)
+    say("random scatter", seed, "fp8" if fp8 else str(dtype), f"Hkv={Hkv} D={D} B={B} NB={NB} T={T}")
+    if fp8:
+        pool = workloads.new_pool(1, NB, Hkv, B, D, torch.uint8, DEV)
+        pool.copy_(torch.randint(0, 256, pool.shape, generator=gen, device=DEV, dtype=torch.uint8))
+        k, v = (p[0] for p in workloads.planes(pool))
+        kb, vb = codes(k), codes(v)
+        ks, vs = 0.25, 0.5
+        oracle.reshape_and_cache8(kb, vb, key.cpu(), value.cpu(), oracle.BF16 if dtype ==
+                                  torch.bfloat16 else oracle.FP16, ks, vs, slots, Hkv, D, B, NB)
+        pkv.reshape_and_cache_fp8(key, value, k, v, sm, NB, ks, vs, B)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes(k), kb), "K pool differs"
+        assert np.array_equal(codes(v), vb), "V pool differs"
+    else:
+        pool = workloads.new_pool(1, NB, Hkv, B, D, dtype, DEV)
+        pool.copy_(workloads.randn(pool.shape, dtype, gen, DEV))
+        k, v = (p[0] for p in workloads.planes(pool))
+        kw, vw = words(k), words(v)
+        oracle.reshape_and_cache(kw, vw, key.cpu(), value.cpu(), slots, Hkv, D, B, NB)
+        pkv.reshape_and_cache(key, value, k, v, sm, NB, B)
+        torch.cuda.synchronize()
+        assert np.array_equal(words(k), kw), "K pool differs"
+        assert np.array_equal(words(v), vw), "V pool differs"
