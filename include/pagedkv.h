@@ -223,6 +223,10 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  *   scale        multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
  *   num_workgroups 0 = library choice (paged_attention_num_workgroups), else the number of
  *                workgroups (1 .. 2^20); results depend on it only through rounding order.
+ *                With the library's choice of a full grid (two per compute unit), a batch of at
+ *                most that many (sequence, kv head, head tile) streams whose lengths do not split
+ *                evenly over it runs on the first half of the grid (one per compute unit), which
+ *                cuts half as many streams; the result is then that of num_workgroups = half.
  *   workspace    device, >= paged_attention_workspace_bytes(...) bytes, 256-byte aligned. Its
  *                last 4 G bytes are arrival counters and the rest is scratch. Zero-fill the whole
  *                buffer once before its first use; every call that completes leaves its counters

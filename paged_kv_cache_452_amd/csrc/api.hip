@@ -418,6 +418,8 @@ pkv_status decode_impl(void* out, const void* q, const void* new_k, const void* 
   a.new_k = new_k;
   a.new_v = new_v;
   a.odd_weight = odd_xcd_weight();
+  a.may_halve = num_workgroups == 0 && grid == pkv::kWorkgroupsPerCU * device_cus() &&
+                (long)num_seqs * num_kv_heads * head_tiles <= grid;
   const float one = 1.0f;
   a.k_inv = one / k_scale;
   a.v_inv = one / v_scale;

@@ -254,9 +254,7 @@ paged_decode_kernel(DecodeLaunch a) {
 
   const int Hh = a.num_kv_heads * a.head_tiles;  // streams per sequence
   const int W = uniform(Hh * s_ps[S]);
-  const int nwg = min((int)gridDim.x, W);
-  const int wg = blockIdx.x;
-  if (wg >= nwg) return;  // uniform over the workgroup
+  int nwg = min((int)gridDim.x, W);
   // Weighted ranges only when they can help and cannot hurt:
   //  * every range keeps at least one position (W >= 2 nwg with weights in [kEvenWeight / 2,
   //    kEvenWeight]): the split-stream bookkeeping needs non-empty ranges;
@@ -264,11 +262,23 @@ paged_decode_kernel(DecodeLaunch a) {
   //    with W / nwg a whole number of streams): then it splits no stream, and any weighting
   //    would add a merge to every workgroup. Every workgroup sees the same plan, so all decide
   //    alike.
-  bool aligned = same_len && W % nwg == 0;
-  if (aligned) {
-    const int L = s_ps[1] - s_ps[0];  // units of every sequence
-    aligned = L > 0 && (W / nwg) % L == 0;
+  auto aligned_for = [&](int n) {
+    bool al = same_len && W % n == 0;
+    if (al) {
+      const int L = s_ps[1] - s_ps[0];  // units of every sequence
+      al = L > 0 && (W / n) % L == 0;
+    }
+    return al;
+  };
+  bool aligned = aligned_for(nwg);
+  // At most as many streams as workgroups, not cut evenly: the full grid would split nearly every
+  // stream; one workgroup per compute unit (the first half of the grid) splits half as many.
+  if (a.may_halve && !aligned && nwg >= 2) {
+    nwg /= 2;
+    aligned = aligned_for(nwg);
   }
+  const int wg = blockIdx.x;
+  if (wg >= nwg) return;  // uniform over the workgroup
   const int odd_w = W >= 2 * nwg && !aligned ? a.odd_weight : kEvenWeight;
   const int r0 = range_start(wg, nwg, W, odd_w);
   const int r1 = range_start(wg + 1, nwg, W, odd_w);

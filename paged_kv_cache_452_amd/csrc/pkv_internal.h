@@ -110,6 +110,8 @@ struct DecodeLaunch {
   float k_inv;          // fp8 pools: 1 / k_scale and 1 / v_scale (the new token's quantization)
   float v_inv;
   int odd_weight;       // range weight of workgroups on odd XCDs (even ones: kEvenWeight)
+  int may_halve;        // the library chose a full grid and there are at most as many streams
+                        // as workgroups: the kernel may use half of them (see the kernel)
 };
 
 // Launch the decode kernel on `grid` workgroups (append: the fused variant that takes each

@@ -410,3 +410,24 @@ def test_split_streams_are_deterministic(num_workgroups):
                          num_workgroups, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), first.view(torch.int16)), f"rep {rep}"
+
+
+def test_default_grid_halves_for_few_uneven_streams():
+    """128 (sequence, kv head) streams of uneven lengths, enough blocks for the full default grid
+    (two workgroups per compute unit): the kernel runs them on the first half of that grid. The
+    result must match the oracle and equal, bit for bit, an explicit grid of that half size."""
+    lens = np.random.default_rng(31).integers(2000, 8001, size=16)
+    spec, t, b = _random_case(32, 8, 128, lens.tolist(), seed=31)
+    k, v = _layer(b)
+    S, maxc = len(lens), int(lens.max())
+    full = pkv.paged_attention_num_workgroups(S, 32, 8, maxc, 16)
+    assert full == 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    say("halved default grid", full)
+    out_default = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, maxc)
+    out_half = gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 32, 8, maxc,
+                          full // 2)
+    torch.cuda.synchronize()
+    assert torch.equal(out_default.view(torch.int16), out_half.view(torch.int16))
+    ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 32, 8,
+                        t.num_blocks)
+    assert_close(out_default, ref, "halved default grid")
