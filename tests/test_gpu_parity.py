@@ -431,3 +431,29 @@ def test_default_grid_halves_for_few_uneven_streams():
     ref = oracle_decode(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 32, 8,
                         t.num_blocks)
     assert_close(out_default, ref, "halved default grid")
+
+
+def test_fused_append_on_halved_default_grid():
+    """The fused step on a batch that runs on half of the default grid: outputs match the oracle
+    and the pools equal the oracle's scatter word for word (the exiting half writes nothing, the
+    working half writes every new token)."""
+    lens = np.random.default_rng(37).integers(2000, 8001, size=16)
+    spec, t, b = _random_case(32, 8, 128, lens.tolist(), seed=37)
+    k, v = _layer(b)
+    _poison_new_slots_(k, v, t, 8, 128, 16)
+    kw, vw = words(k), words(v)
+    oracle.reshape_and_cache(kw, vw, b.new_key.cpu(), b.new_value.cpu(), t.slot_mapping, 8, 128,
+                             16, t.num_blocks)
+    ref = oracle_decode(b.q, None, None, t.block_tables, t.context_lens, spec.scale, 32, 8,
+                        t.num_blocks, k_words=kw, v_words=vw)
+    maxc = int(lens.max())
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(len(lens), 32, 8, 128, 16, maxc),
+                           DEV)
+    out = torch.empty_like(b.q)
+    say("fused append on the halved default grid")
+    pkv.paged_attention_decode_append(out, b.q, b.new_key, b.new_value, k, v, b.block_tables,
+                                      b.context_lens, spec.scale, 32, 8, 128, 16, maxc, 0, ws)
+    torch.cuda.synchronize()
+    assert_close(out, ref, "fused append, halved grid")
+    assert np.array_equal(words(k), kw), "K pool differs from reshape_and_cache's"
+    assert np.array_equal(words(v), vw), "V pool differs from reshape_and_cache's"
