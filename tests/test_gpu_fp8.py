@@ -265,3 +265,23 @@ def test_fused_append_decode_fp8_matches_oracle(Hq, Hkv, D, lens, B, nwg):
     ref_mag = float(np.max(np.abs(ref)))
     err = float(np.max(np.abs(got - ref)))
     assert rel <= 2e-3 and err <= 1e-2 * max(1.0, ref_mag / 2), (rel, err, ref_mag)
+
+
+def test_decode_fp8_on_halved_default_grid():
+    """fp8 pools, a batch that runs on half of the default grid (128 uneven streams): equal bit
+    for bit to an explicit half grid, and within the bar of the oracle."""
+    lens = np.random.default_rng(41).integers(2000, 8001, size=16).tolist()
+    spec, t, b = _case8(32, 8, 128, lens, seed=41)
+    k, v = b.k_pool[0], b.v_pool[0]
+    maxc = int(max(lens))
+    full = pkv.paged_attention_num_workgroups(len(lens), 32, 8, maxc, 16)
+    say("decode fp8 on the halved default grid", full)
+    out_default = gpu_decode8(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 0.75, 0.5,
+                              32, 8, maxc)
+    out_half = gpu_decode8(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 0.75, 0.5,
+                           32, 8, maxc, full // 2)
+    torch.cuda.synchronize()
+    assert torch.equal(out_default.view(torch.int16), out_half.view(torch.int16))
+    ref = oracle_decode8(b.q, k, v, t.block_tables, t.context_lens, spec.scale, 0.75, 0.5, 32, 8,
+                         t.num_blocks)
+    assert_close(out_default, ref, "fp8, halved default grid")
