@@ -255,6 +255,7 @@ paged_decode_kernel(DecodeLaunch a) {
   const int Hh = a.num_kv_heads * a.head_tiles;  // streams per sequence
   const int W = uniform(Hh * s_ps[S]);
   int nwg = min((int)gridDim.x, W);
+  if (nwg == 0) return;  // no positions at all (every sequence empty): uniform over the launch
   // Weighted ranges only when they can help and cannot hurt:
   //  * every range keeps at least one position (W >= 2 nwg with weights in [kEvenWeight / 2,
   //    kEvenWeight]): the split-stream bookkeeping needs non-empty ranges;
