@@ -457,3 +457,17 @@ def test_fused_append_on_halved_default_grid():
     assert_close(out, ref, "fused append, halved grid")
     assert np.array_equal(words(k), kw), "K pool differs from reshape_and_cache's"
     assert np.array_equal(words(v), vw), "V pool differs from reshape_and_cache's"
+
+
+@pytest.mark.parametrize("num_workgroups", [0, 1, 600])
+def test_all_sequences_empty(num_workgroups):
+    """Every context empty: no block positions at all. Each output row is zero (written over a
+    non-zero fill), and the call completes with the default grid, one workgroup or many."""
+    spec, t, b = _random_case(16, 4, 128, [0, 0, 0, 0, 0], seed=43)
+    k, v = _layer(b)
+    out = torch.full_like(b.q, 7.0)
+    say("all sequences empty", num_workgroups)
+    gpu_decode(b.q, k, v, b.block_tables, b.context_lens, spec.scale, 16, 4, 1, num_workgroups,
+               out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
