@@ -139,12 +139,39 @@ def cpu_baseline(batch, spec, layers, budget_s=15.0, kv_scales=None):
         n_layers += 1
         if cpu_s >= budget_s:
             break
+    # The same oracle on one thread, over every head of the first sequences of the last layer
+    # (about 100 MB of K/V), for the per-core rate.
+    lens = np.asarray(t.context_lens)
+    n_seq = 1
+    while n_seq < len(lens) and algorithmic_bytes(lens[:n_seq], spec.num_q_heads,
+                                                  spec.num_kv_heads, spec.head_dim,
+                                                  block=spec.block_size,
+                                                  kv_elem=1 if kv_scales else 2) < 100e6:
+        n_seq += 1
+    pairs = [(s, h) for s in range(n_seq) for h in range(spec.num_q_heads)]
+    one_bytes = algorithmic_bytes(lens[:n_seq], spec.num_q_heads, spec.num_kv_heads,
+                                  spec.head_dim, block=spec.block_size,
+                                  kv_elem=1 if kv_scales else 2)
+    t0 = time.perf_counter()
+    if kv_scales:
+        oracle.paged_decode8(q, kw, vw, kv_scales[0], kv_scales[1], t.block_tables,
+                             t.context_lens, spec.scale, spec.num_q_heads, spec.num_kv_heads,
+                             spec.head_dim, spec.block_size, t.num_blocks, qdt, pairs=pairs,
+                             threads=1)
+    else:
+        oracle.paged_decode(q, kw, vw, t.block_tables, t.context_lens, spec.scale,
+                            spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size,
+                            t.num_blocks, qdt, pairs=pairs, threads=1)
+    one_s = time.perf_counter() - t0
     return {"value": round(done_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n_layers} whole layer(s) of the same batch ({spec.num_seqs} seqs x "
                       f"{spec.num_q_heads} heads each), fp64, timed from host-resident pools; "
                       f"device-to-host copy {d2h_s:.2f} s not included",
-            "seconds": round(cpu_s, 3)}
+            "seconds": round(cpu_s, 3),
+            "single_thread": {"value": round(one_bytes / one_s / 1e9, 4), "unit": "GB/s",
+                              "cores": 1, "sample": f"every head of the first {n_seq} "
+                              f"sequence(s) of one layer", "seconds": round(one_s, 3)}}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3) -> int:
