@@ -387,13 +387,20 @@ paged_decode_kernel(DecodeLaunch a) {
   auto window_load = [&](int c) -> Win {
     const int p = r0 + wave + kWaves * (64 * c + lane);
     if (p >= r1) return Win{0u, 0u};
-    const int s = seq_of(p);
-    const int pb = s_ps[s];
-    const int nb = s_ps[s + 1] - pb;
-    const int r = p - Hh * pb;
-    const int gh = r / nb;
-    const int j = r - gh * nb;
-    const int g = gh / a.head_tiles;
+    int s, j, g;
+    if (p >= cur.start && p < cur.end) {  // in the current stream: no search, no divisions
+      s = cur.s;
+      j = p - cur.start;
+      g = cur.gh / a.head_tiles;
+    } else {
+      s = seq_of(p);
+      const int pb = s_ps[s];
+      const int nb = s_ps[s + 1] - pb;
+      const int r = p - Hh * pb;
+      const int gh = r / nb;
+      j = r - gh * nb;
+      g = gh / a.head_tiles;
+    }
     // 16-token unit j of the stream: sub-tile j % R of physical block block_tables[s][j / R]
     // (R = block_size / 16 sub-tiles per block, each 16 * D elements of the block's tile). Tiles
     // of one plane lie two apart (the K and V tiles of a (block, head) alternate), so the K and V
