@@ -5,7 +5,10 @@
 // flattened space of W = sum_s nb_s * (kv heads * head tiles) block positions, and the launch's
 // workgroups cut that space into contiguous ranges: equal ones, or (when the equal cut would split
 // streams anyway) ranges weighted by the XCD a workgroup runs on, since odd-numbered XCDs stream
-// measurably slower (see range_start). A workgroup's share is thus fixed whatever the mix of
+// measurably slower (see range_start). When the library chose the full grid and the batch has no
+// more streams than workgroups, of uneven lengths, only the first half of the workgroups (one
+// per compute unit) take ranges, which halves the streams the cut splits. A workgroup's share is
+// thus fixed whatever the mix of
 // context lengths: a 32k-token sequence is spread over many workgroups and a batch of short ones
 // is packed into few, with no per-sequence partition size to tune and no tail of idle compute
 // units. Each workgroup derives the plan itself from context_lens (a prefix sum in LDS), so the
