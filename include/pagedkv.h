@@ -2,8 +2,8 @@
  * pagedkv.h — C ABI of libpagedkv: PagedAttention decode on AMD Instinct MI355X (gfx950).
  *
  * The library implements the decode step of paged attention. A sequence's keys and values live in
- * fixed-size blocks of `block_size` tokens, scattered over one shared physical block pool; a
- * per-sequence block table maps logical block j (tokens j*B .. j*B+B-1) to a physical block id.
+ * fixed-size blocks of `block_size` tokens, scattered over one shared physical block pool; row s
+ * of the block tables holds, at entry j, the physical block id of tokens j*B .. j*B+B-1.
  * The attention kernel takes the block table as an argument and gathers K and V through it in
  * place, with no staging copy into contiguous memory.
  *   - "KV-Cache Management and PagedAttention" (adversariallm.ai), section
@@ -13,7 +13,8 @@
  *     "PagedAttention: OS Virtual Memory Architecture for GPUs" (physical pool, block table),
  *     "How Block Paging Operates During Generation" (boundary allocation; block byte size spans
  *     all layers) and "Under the Hood: The PagedAttention CUDA Kernel"
- *     (physical_block_id = block_table[seq_id, logical_block_id]; softmax over the gathered keys).
+ *     (the kernel resolves each logical block through the table, then takes the softmax over the
+ *     keys it gathered).
  *
  * Conventions for every entry point
  *   - Device pointers are HIP device addresses owned by the caller. The library never allocates
@@ -126,17 +127,29 @@ size_t kv_pool_bytes(int num_layers, int num_blocks, int num_kv_heads, int head_
                      pkv_dtype dtype);
 
 /*
- * Describe a caller-allocated pool (`bytes` bytes at `base`, laid out as above). Checks:
- * non-NULL, 256-byte aligned base, bytes >= kv_pool_bytes(...), supported shape. On success *out
- * receives a new host object (free it with kv_pool_destroy). The memory stays owned by the caller
- * and must outlive the object. No device work is done.
+ * Describe a caller-allocated pool (`bytes` bytes at `base`, laid out as above): the one shared
+ * pool of fixed-size physical blocks that every sequence's table points into ("PagedAttention and
+ * KV Cache Management", section "PagedAttention: OS Virtual Memory Architecture for GPUs": the
+ * cache is carved into equal blocks in one physical pool; "KV-Cache Management and
+ * PagedAttention", section "PagedAttention: treat the cache like virtual memory": any free block
+ * can hold any sequence's tokens). One block id names the same slot range in every layer, as
+ * the block byte size in "How Block Paging Operates During Generation" (item 3) spans all layers.
+ * Checks: non-NULL, 256-byte aligned base, bytes >= kv_pool_bytes(...), supported shape. On
+ * success *out receives a new host object (free it with kv_pool_destroy). The memory stays owned
+ * by the caller and must outlive the object. No device work is done.
+ * Errors: PKV_ERR_INVALID_ARG (NULL out or base, non-positive size, bytes too small, host
+ * allocation failure), PKV_ERR_UNSUPPORTED (head_dim, block_size or dtype), PKV_ERR_ALIGNMENT.
  */
 pkv_status kv_pool_create(pkv_pool** out, void* base, size_t bytes, int num_layers,
                           int num_blocks, int num_kv_heads, int head_dim, int block_size,
                           pkv_dtype dtype);
 
 /* Addresses of layer `layer`'s K and V planes: k_layer = base + layer * (kv_pool_bytes / layers),
- * v_layer = k_layer + one tile (block_size * head_dim elements). */
+ * v_layer = k_layer + one tile (block_size * head_dim elements). Each layer keeps its own keys and
+ * values for the same block ids ("KV-Cache Management and PagedAttention", section "Why the cache
+ * exists, and why it's so hungry": one key and one value vector per token, head and layer).
+ * The decode and scatter calls take these two addresses. PKV_ERR_INVALID_ARG for a NULL argument
+ * or a layer outside [0, num_layers); nothing is written then. */
 pkv_status kv_pool_layer(const pkv_pool* pool, int layer, void** k_layer, void** v_layer);
 
 /* Frees the host object (NULL is a no-op). Does not touch device memory. */
@@ -194,7 +207,11 @@ int paged_attention_num_workgroups(int num_seqs, int num_q_heads, int num_kv_hea
                                    int max_context_len, int block_size);
 
 /*
- * Workspace bytes paged_attention_decode needs for these arguments: with G workgroups
+ * Workspace bytes paged_attention_decode needs for these arguments. The workspace holds the
+ * partial softmax state of sequences whose blocks are split between workgroups ("PagedAttention
+ * and KV Cache Management", section "Under the Hood: The PagedAttention CUDA Kernel": slices of
+ * a sequence's logical blocks are processed separately and their softmax reductions combined
+ * into one output). With G workgroups
  * (num_workgroups, or the library's choice when it is 0),
  *     bytes = G * 2 * 16 * (head_dim + 2) * 4 + roundup(4 G, 256)
  * (fp32 partials of at most two split streams per workgroup, then G arrival counters).

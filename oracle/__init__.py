@@ -67,6 +67,8 @@ def _load():
     lib.oracle_paged_decode8.restype = i
     lib.oracle_reshape_and_cache8.argtypes = [p, p, p, p, i, f, f, p, i, i, i, i, lg]
     lib.oracle_reshape_and_cache8.restype = i
+    lib.oracle_dead_slot_indices.argtypes = [i, i, p, p, i, i, i, i, i, p, lg]
+    lib.oracle_dead_slot_indices.restype = lg
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     _lib = lib
@@ -108,6 +110,21 @@ def pool_index(is_v: bool, block: int, kv_head: int, slot: int, dim: int,
     """Element index of (block, kv head, token slot, dim) in one layer's K or V pool."""
     return int(_load().oracle_pool_index(int(bool(is_v)), block, kv_head, slot, dim,
                                          num_kv_heads, block_size, head_dim))
+
+
+def dead_slot_indices(is_v: bool, fp8: bool, block_tables, context_lens, num_kv_heads: int,
+                      block_size: int, head_dim: int) -> np.ndarray:
+    """int64 pool indices (pool_index / pool_index8) of every dead slot: slots n mod B .. B-1
+    of each sequence's partly filled last block, all kv heads and dims."""
+    bt, cl = _i32(block_tables), _i32(context_lens)
+    S = cl.shape[0]
+    mb = bt.shape[1] if bt.ndim == 2 else 0
+    args = (int(bool(is_v)), int(bool(fp8)), _ptr(bt), _ptr(cl), S, mb, num_kv_heads, block_size,
+            head_dim)
+    n = int(_load().oracle_dead_slot_indices(*args, None, 0))
+    out = np.zeros(max(n, 1), np.int64)
+    _load().oracle_dead_slot_indices(*args, _ptr(out), n)
+    return out[:n]
 
 
 def gather(k_pool, v_pool, dtype: int, table, n: int, kv_head: int, num_kv_heads: int,

@@ -11,16 +11,17 @@
  *
  * What it computes
  *   1. Gather ("PagedAttention and KV Cache Management" (blog.sejan.dev), section "Under the
- *      Hood: The PagedAttention CUDA Kernel": physical_block_id = block_table[seq_id,
- *      logical_block_id]; "KV-Cache Management and PagedAttention" (adversariallm.ai), section
- *      "PagedAttention: treat the cache like virtual memory"): token t of sequence s is slot
+ *      Hood: The PagedAttention CUDA Kernel": the kernel maps a sequence's logical block to
+ *      its physical block through the table; "KV-Cache Management and PagedAttention"
+ *      (adversariallm.ai), section "PagedAttention: treat the cache like virtual memory"):
+ *      token t of sequence s is slot
  *      t mod B of physical block block_table[s][floor(t / B)]. The sequence's keys and values
  *      are reassembled into contiguous order K_c[t], V_c[t], t = 0 .. n-1 — the layout paging
  *      replaced ("PagedAttention and KV Cache Management", section "The Memory Fragmentation
  *      Crisis in Traditional Serving").
  *   2. Dense attention of one query over those rows ("KV-Cache Management and PagedAttention",
- *      section "Why the cache exists, and why it's so hungry": the new token attends to every
- *      previous token): x_t = scale * q.K_c[t]; m = max_t x_t; w_t = exp(x_t - m);
+ *      section "Why the cache exists, and why it's so hungry": a decode step's query is scored
+ *      against all cached keys of its sequence): x_t = scale * q.K_c[t]; m = max_t x_t; w_t = exp(x_t - m);
  *      out = sum_t w_t V_c[t] / sum_t w_t. Query head h reads kv head h / (Hq / Hkv)
  *      (grouped-query attention, "PagedAttention and KV Cache Management", section "The KV
  *      Cache Size Equation": n_kv_heads << n_q_heads; contiguous groups are this oracle's
@@ -393,6 +394,33 @@ int oracle_reshape_and_cache(uint16_t* k_pool, uint16_t* v_pool, const uint16_t*
     }
   }
   return 0;
+}
+
+/*
+ * Pool indices of the dead slots of every sequence: slots t = n mod B .. B-1 of the block that
+ * holds its last token, when that block is partly filled, for every kv head and dim (the slots a
+ * decode must never read: "PagedAttention and KV Cache Management", section "How Block Paging
+ * Operates During Generation": only the last block of a sequence is partly used). fp8 selects
+ * pool_index8. Writes at most cap indices to out (out may be NULL) and returns how many there are.
+ */
+long oracle_dead_slot_indices(int is_v, int fp8, const int32_t* block_tables,
+                              const int32_t* context_lens, int S, int max_blocks, int Hkv, int B,
+                              int D, long* out, long cap) {
+  long k = 0;
+  for (int s = 0; s < S; ++s) {
+    int n = context_lens[s];
+    if (n <= 0 || n % B == 0) continue;
+    long b = block_tables[(size_t)s * (size_t)max_blocks + (size_t)(n / B)];
+    for (int t = n % B; t < B; ++t)
+      for (int h = 0; h < Hkv; ++h)
+        for (int d = 0; d < D; ++d) {
+          if (out != NULL && k < cap)
+            out[k] = (long)(fp8 ? pool_index8(is_v, b, h, t, d, Hkv, B, D)
+                                : pool_index(is_v, b, h, t, d, Hkv, B, D));
+          ++k;
+        }
+  }
+  return k;
 }
 
 int oracle_max_threads(void) {

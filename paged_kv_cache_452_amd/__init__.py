@@ -153,6 +153,84 @@ def _require_cuda(*tensors) -> None:
             raise ValueError("device tensors required (the library runs on the GPU only)")
 
 
+# Argument checks of the bindings. The kernels take raw addresses and trust the element types,
+# shapes and the dense row-major layout of what they index: an int64 block table or a sliced view
+# read as int32 would send table padding or the wrong rows into the pool walk. Every check runs
+# before any launch and raises ValueError.
+
+def _int_tensor(name: str, t, dtype, ndim: int, rows: Optional[int] = None,
+                address_ok: bool = False):
+    import torch
+    if isinstance(t, int) and address_ok:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a tensor or a device address")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: element type {t.dtype}, expected {dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: {t.dim()} dimensions, expected {ndim}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if rows is not None and t.shape[0] != rows:
+        raise ValueError(f"{name}: {t.shape[0]} rows, expected {rows}")
+
+
+def _rows(name: str, t, shape, dtype=None):
+    """A dense [..] tensor of 16-bit elements with exactly `shape` (and `dtype`, when given)."""
+    import torch
+    if isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a tensor or a device address")
+    if t.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"{name}: element type {t.dtype}, expected bfloat16 or float16")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: element type {t.dtype}, expected {dtype} (as q / key)")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _plane(name: str, t, dtype):
+    """A pool plane: a view whose last dimension is dense (the K or V tiles of one layer), of the
+    pool's element type."""
+    import torch
+    if isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a tensor or a device address")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: element type {t.dtype}, expected {dtype}")
+    if t.dim() == 0 or (t.shape[-1] > 1 and t.stride(-1) != 1):
+        raise ValueError(f"{name}: the last dimension must be dense")
+
+
+def _workspace(t):
+    import torch
+    if t is None or isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError("workspace: must be a contiguous tensor")
+
+
+def _decode_args(name, out, q, k_pool, v_pool, block_tables, context_lens, num_q_heads,
+                 head_dim, pool_dtype=None):
+    """Checks shared by the decode bindings. Returns the number of sequences."""
+    import torch
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError(f"{name}: q must be a tensor [num_seqs][num_q_heads][head_dim]")
+    S = q.shape[0]
+    _rows("q", q, (S, num_q_heads, head_dim))
+    _rows("out", out, (S, num_q_heads, head_dim), q.dtype)
+    pd = q.dtype if pool_dtype is None else pool_dtype
+    _plane("k_pool", k_pool, pd)
+    _plane("v_pool", v_pool, pd)
+    _int_tensor("block_tables", block_tables, torch.int32, 2, S)
+    _int_tensor("context_lens", context_lens, torch.int32, 1, S)
+    return S
+
+
 def pkv_status_string(status: int) -> str:
     return load_library().pkv_status_string(status).decode()
 
@@ -213,8 +291,16 @@ def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, num_blocks: int,
                       block_size: int = 16, stream=None) -> None:
     """Scatter key/value [T][Hkv][D] into the pool slots named by slot_mapping (int64 [T]).
     k_pool / v_pool: one layer's K and V planes, as tensors (views) or device addresses."""
-    _require_cuda(key, value, k_pool, v_pool, slot_mapping)
+    import torch
+    if not isinstance(key, torch.Tensor) or key.dim() != 3:
+        raise ValueError("key must be a tensor [num_tokens][num_kv_heads][head_dim]")
     T, Hkv, D = key.shape
+    _rows("key", key, (T, Hkv, D))
+    _rows("value", value, (T, Hkv, D), key.dtype)
+    _plane("k_pool", k_pool, key.dtype)
+    _plane("v_pool", v_pool, key.dtype)
+    _int_tensor("slot_mapping", slot_mapping, torch.int64, 1, T, address_ok=True)
+    _require_cuda(key, value, k_pool, v_pool, slot_mapping)
     _check("reshape_and_cache", load_library().reshape_and_cache(
         _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping), T, Hkv, D,
         block_size, num_blocks, _dtype_code(key), _stream(stream)))
@@ -251,9 +337,11 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
                            max_context_len: int, num_workgroups: int = 0, workspace=None,
                            stream=None) -> None:
     """out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s over each sequence's paged K/V."""
+    S = _decode_args("paged_attention_decode", out, q, k_pool, v_pool, block_tables,
+                     context_lens, num_q_heads, head_dim)
+    _workspace(workspace)
     _require_cuda(out, q, k_pool, v_pool, block_tables, context_lens, workspace)
-    S = q.shape[0]
-    max_blocks = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    max_blocks = block_tables.shape[1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("paged_attention_decode", load_library().paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
@@ -267,8 +355,16 @@ def reshape_and_cache_fp8(key, value, k_pool, v_pool, slot_mapping, num_blocks: 
                           stream=None) -> None:
     """Quantize key/value [T][Hkv][D] (bf16/fp16) to E4M3 and scatter them into one layer's fp8
     pools (uint8 tensors or device addresses) at the slots named by slot_mapping."""
-    _require_cuda(key, value, k_pool, v_pool, slot_mapping)
+    import torch
+    if not isinstance(key, torch.Tensor) or key.dim() != 3:
+        raise ValueError("key must be a tensor [num_tokens][num_kv_heads][head_dim]")
     T, Hkv, D = key.shape
+    _rows("key", key, (T, Hkv, D))
+    _rows("value", value, (T, Hkv, D), key.dtype)
+    _plane("k_pool", k_pool, torch.uint8)
+    _plane("v_pool", v_pool, torch.uint8)
+    _int_tensor("slot_mapping", slot_mapping, torch.int64, 1, T, address_ok=True)
+    _require_cuda(key, value, k_pool, v_pool, slot_mapping)
     _check("reshape_and_cache_fp8", load_library().reshape_and_cache_fp8(
         _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping), T, Hkv, D,
         block_size, num_blocks, _dtype_code(key), float(k_scale), float(v_scale),
@@ -281,9 +377,12 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, block_tables, context_len
                                max_context_len: int, num_workgroups: int = 0, workspace=None,
                                stream=None) -> None:
     """paged_attention_decode over fp8 (E4M3) pools with per-pool scales."""
+    import torch
+    S = _decode_args("paged_attention_decode_fp8", out, q, k_pool, v_pool, block_tables,
+                     context_lens, num_q_heads, head_dim, pool_dtype=torch.uint8)
+    _workspace(workspace)
     _require_cuda(out, q, k_pool, v_pool, block_tables, context_lens, workspace)
-    S = q.shape[0]
-    max_blocks = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    max_blocks = block_tables.shape[1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("paged_attention_decode_fp8", load_library().paged_attention_decode_fp8(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
@@ -320,9 +419,15 @@ def paged_attention_decode_append(out, q, key, value, k_pool, v_pool, block_tabl
     """One fused decode step: each sequence's newest token (key/value [S][Hkv][D], at position
     context_lens[s] - 1) is written into the pool and attended to with the rest of the context.
     kv_scales=(k_scale, v_scale) for fp8 pools."""
+    import torch
+    S = _decode_args("paged_attention_decode_append", out, q, k_pool, v_pool, block_tables,
+                     context_lens, num_q_heads, head_dim,
+                     pool_dtype=None if kv_scales is None else torch.uint8)
+    _rows("key", key, (S, num_kv_heads, head_dim), q.dtype)
+    _rows("value", value, (S, num_kv_heads, head_dim), q.dtype)
+    _workspace(workspace)
     _require_cuda(out, q, key, value, k_pool, v_pool, block_tables, context_lens, workspace)
-    S = q.shape[0]
-    max_blocks = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    max_blocks = block_tables.shape[1]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
     if kv_scales is None:
@@ -345,6 +450,9 @@ def paged_attention_decode_append(out, q, key, value, k_pool, v_pool, block_tabl
 def copy_blocks(pool: "KVPool", src_blocks, dst_blocks, stream=None) -> None:
     """Copy blocks src_blocks[i] -> dst_blocks[i] (device int32 tensors) in every layer of the
     pool's K and V (the device half of copy-on-write)."""
+    import torch
+    for name, t in (("src_blocks", src_blocks), ("dst_blocks", dst_blocks)):
+        _int_tensor(name, t, torch.int32, 1, address_ok=True)
     _require_cuda(src_blocks, dst_blocks)
     n = int(src_blocks.numel())
     if int(dst_blocks.numel()) != n:

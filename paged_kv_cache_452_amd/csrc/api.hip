@@ -85,13 +85,19 @@ bool device_visible(const int32_t* p, const int32_t** dev) {
 }
 
 // Range weight of decode workgroups on odd-numbered XCDs (even ones weigh pkv::kEvenWeight): the
-// default below, or PKV_ODD_XCD_WEIGHT from the environment (read at every call), clamped to
-// [kEvenWeight / 2, kEvenWeight].
+// default below, or PKV_ODD_XCD_WEIGHT from the environment, clamped to
+// [kEvenWeight / 2, kEvenWeight]. Read once, at the first decode call of the process: the weight
+// moves the range boundaries and with them the rounding order of split streams, so every call of
+// one process must use the same value for its results to be reproducible.
 constexpr int kDefaultOddXcdWeight = 900;
 int odd_xcd_weight() {
-  int v = kDefaultOddXcdWeight;
-  if (const char* e = getenv("PKV_ODD_XCD_WEIGHT")) v = atoi(e);
-  return v < pkv::kEvenWeight / 2 ? pkv::kEvenWeight / 2 : v > pkv::kEvenWeight ? pkv::kEvenWeight : v;
+  static const int weight = [] {
+    int v = kDefaultOddXcdWeight;
+    if (const char* e = getenv("PKV_ODD_XCD_WEIGHT")) v = atoi(e);
+    return v < pkv::kEvenWeight / 2 ? pkv::kEvenWeight / 2
+                                    : v > pkv::kEvenWeight ? pkv::kEvenWeight : v;
+  }();
+  return weight;
 }
 
 // Bytes of one block's region in one layer: the K and V tiles of all its kv heads.

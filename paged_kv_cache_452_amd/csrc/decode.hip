@@ -16,9 +16,9 @@
 //
 // Inside a range the four wavefronts interleave block by block (wave i takes positions
 // r0 + i, r0 + i + 4, ...), so all four always work on the same stream. Per 16-token block a
-// wavefront follows the block table ("PagedAttention and KV Cache Management"
-// (blog.sejan.dev), section "Under the Hood: The PagedAttention CUDA Kernel":
-// physical_block_id = block_table[seq_id, logical_block_id]) and:
+// wavefront looks up the block's physical id in the sequence's block table, row s, entry j / R
+// for unit j of the stream (R = 16-token units per block; "PagedAttention and KV Cache
+// Management" (blog.sejan.dev), section "Under the Hood: The PagedAttention CUDA Kernel"), and:
 //   * reads the K tile and the V tile straight from the pool: 64 lanes x 16 bytes per load
 //     instruction, each instruction one contiguous 1 KiB range; the pool's tile order makes
 //     every lane's 16 bytes a ready matrix-core operand, so nothing is staged or shuffled;

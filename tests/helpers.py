@@ -90,23 +90,11 @@ def poison_dead_slots_(k_layer: torch.Tensor, v_layer: torch.Tensor, tables, len
                        num_kv_heads: int, head_dim: int, block_size: int = 16):
     """Write NaN into the unwritten slots (t >= n) of every sequence's last block, locating
     them with the oracle's layout function."""
-    B = block_size
-    idx = []
-    for s, n in enumerate(lens):
-        n = int(n)
-        if n % B == 0:
-            continue
-        b = int(tables[s][n // B])
-        for t in range(n % B, B):
-            for h in range(num_kv_heads):
-                for d in range(head_dim):
-                    idx.append((oracle.pool_index(False, b, h, t, d, num_kv_heads, B, head_dim),
-                                oracle.pool_index(True, b, h, t, d, num_kv_heads, B, head_dim)))
-    if not idx:
-        return
-    ia = torch.tensor(idx, dtype=torch.long, device=k_layer.device)
-    set_plane_(k_layer, ia[:, 0], float("nan"))
-    set_plane_(v_layer, ia[:, 1], float("nan"))
+    for plane, is_v in ((k_layer, False), (v_layer, True)):
+        idx = oracle.dead_slot_indices(is_v, False, tables, lens, num_kv_heads, block_size,
+                                       head_dim)
+        if idx.size:
+            set_plane_(plane, torch.from_numpy(idx).to(plane.device), float("nan"))
 
 
 # ---- fp8 (E4M3) pools ----------------------------------------------------------------------
@@ -146,20 +134,35 @@ def oracle_decode8(q, k_layer, v_layer, block_tables, context_lens, scale, k_sca
 def poison_dead_slots8_(k_layer: torch.Tensor, v_layer: torch.Tensor, tables, lens,
                         num_kv_heads: int, head_dim: int, block_size: int = 16):
     """Write the E4M3 NaN code into the unwritten slots of every sequence's last block."""
-    B = block_size
-    idx = []
-    for s, n in enumerate(lens):
-        n = int(n)
-        if n % B == 0:
-            continue
-        b = int(tables[s][n // B])
-        for t in range(n % B, B):
-            for h in range(num_kv_heads):
-                for d in range(head_dim):
-                    idx.append((oracle.pool_index8(False, b, h, t, d, num_kv_heads, B, head_dim),
-                                oracle.pool_index8(True, b, h, t, d, num_kv_heads, B, head_dim)))
-    if not idx:
-        return
-    ia = torch.tensor(idx, dtype=torch.long, device=k_layer.device)
-    set_plane_(k_layer, ia[:, 0], 0x7F)
-    set_plane_(v_layer, ia[:, 1], 0x7F)
+    for plane, is_v in ((k_layer, False), (v_layer, True)):
+        idx = oracle.dead_slot_indices(is_v, True, tables, lens, num_kv_heads, block_size,
+                                       head_dim)
+        if idx.size:
+            set_plane_(plane, torch.from_numpy(idx).to(plane.device), 0x7F)
+
+
+class LayerHost:
+    """A reused pinned host buffer for one layer of a pool ([blocks][kv heads][K, V][tile]):
+    device-to-host copies of whole layers, and their K and V planes as contiguous raw words (the
+    form the oracle takes)."""
+
+    def __init__(self, layer: torch.Tensor):
+        self.buf = torch.empty(layer.shape, dtype=layer.dtype, pin_memory=True)
+
+    def fetch(self, layer: torch.Tensor) -> np.ndarray:
+        """Copy a layer (device) into the buffer; returns its raw words (uint16, or uint8 for fp8
+        pools) as a [blocks][kv heads][2][tile] numpy view of the buffer."""
+        self.buf.copy_(layer)
+        if self.buf.dtype == torch.uint8:
+            return self.buf.numpy()
+        return self.buf.view(torch.int16).numpy().view(np.uint16)
+
+    def planes(self, layer: torch.Tensor):
+        """Contiguous copies of the layer's K and V planes (raw words)."""
+        h = self.fetch(layer)
+        return np.ascontiguousarray(h[:, :, 0, :]), np.ascontiguousarray(h[:, :, 1, :])
+
+    def equals(self, layer: torch.Tensor, kw: np.ndarray, vw: np.ndarray) -> bool:
+        """The device layer's K and V planes equal kw and vw word for word."""
+        h = self.fetch(layer)
+        return bool(np.array_equal(h[:, :, 0, :], kw) and np.array_equal(h[:, :, 1, :], vw))
