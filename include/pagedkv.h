@@ -452,6 +452,39 @@ pkv_status paged_attention_decode_append_fp8(void* out, const void* q, const voi
                                              pkv_dtype dtype, void* workspace,
                                              size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Bytes of the library's own decode scratch on each device (see paged_attention_decode_noalloc):
+ * the workspace of 1024 workgroups at head_dim 128.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES 17043456
+
+/*
+ * paged_attention_decode for callers that cannot allocate device memory: code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc. Same arguments, result
+ * and errors as paged_attention_decode (16-bit pools), but no workspace argument: the split-stream
+ * partials and arrival counters live in a static device array of PKV_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on each device it runs on until the process ends. The call allocates
+ * nothing (no hipMalloc, no library allocation) and does not synchronise.
+ *   - Limit: paged_attention_workspace_bytes(...) for these arguments (with the library's grid
+ *     choice when num_workgroups is 0) must not exceed PKV_NOALLOC_SCRATCH_BYTES, i.e. at most
+ *     1024 workgroups at head_dim 128 (about 2000 at 64); larger requests return
+ *     PKV_ERR_WORKSPACE and launch nothing. The library's default grid (two workgroups per compute
+ *     unit) always fits on MI355X.
+ *   - The first call on a device looks up the array's device address and clears its arrival
+ *     counters with a small kernel on `stream`; every completed call leaves them zero again.
+ *   - All calls on one device share the one array: calls that may overlap in time on the same
+ *     device (different streams, or one graph replayed concurrently with another call) race and
+ *     give wrong results. Calls ordered on one stream are safe.
+ * Returns PKV_ERR_HIP if the array cannot be located on the current device.
+ */
+pkv_status paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_tables,
+                                          const int32_t* context_lens, float scale,
+                                          int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int num_seqs, int max_blocks_per_seq,
+                                          int max_context_len, int num_workgroups,
+                                          pkv_dtype dtype, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(pkv_status status);
 

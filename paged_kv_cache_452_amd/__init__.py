@@ -29,7 +29,10 @@ EXPORTED = ("kv_pool_bytes", "kv_pool_create", "kv_pool_layer", "kv_pool_destroy
             "kv_block_manager_create", "kv_block_manager_destroy", "kv_block_manager_num_free",
             "kv_block_manager_allocate", "kv_block_manager_fork", "kv_block_manager_append",
             "kv_block_manager_release", "kv_block_manager_tables", "kv_block_manager_num_free_host",
-            "kv_block_manager_swap_out", "kv_block_manager_swap_in", "pkv_status_string")
+            "kv_block_manager_swap_out", "kv_block_manager_swap_in", "pkv_status_string",
+            "paged_attention_decode_noalloc")
+
+PKV_NOALLOC_SCRATCH_BYTES = 17043456  # include/pagedkv.h
 
 PKV_ERR_NO_BLOCKS = -6
 
@@ -80,6 +83,9 @@ def load_library(build_if_missing: bool = True):
     lib.paged_attention_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f, i, i, i, i, i,
                                                   i, i, i, i, vp, sz, vp]
     lib.paged_attention_decode_append.restype = i
+    lib.paged_attention_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i,
+                                                   i, i, vp]
+    lib.paged_attention_decode_noalloc.restype = i
     lib.paged_attention_decode_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f, f, f, i,
                                                       i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.paged_attention_decode_append_fp8.restype = i
@@ -347,6 +353,23 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
         float(scale), num_q_heads, num_kv_heads, head_dim, block_size, S, max_blocks,
         max_context_len, num_workgroups, _dtype_code(q), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens,
+                                   scale: float, num_q_heads: int, num_kv_heads: int,
+                                   head_dim: int, block_size: int, max_context_len: int,
+                                   num_workgroups: int = 0, stream=None) -> None:
+    """paged_attention_decode without a workspace: the library's own per-device scratch holds the
+    split-stream state, so the call allocates nothing. Calls that overlap in time on one device
+    race (they share that scratch); calls ordered on one stream are safe."""
+    S = _decode_args("paged_attention_decode_noalloc", out, q, k_pool, v_pool, block_tables,
+                     context_lens, num_q_heads, head_dim)
+    _require_cuda(out, q, k_pool, v_pool, block_tables, context_lens)
+    _check("paged_attention_decode_noalloc", load_library().paged_attention_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+        float(scale), num_q_heads, num_kv_heads, head_dim, block_size, S,
+        block_tables.shape[1], max_context_len, num_workgroups, _dtype_code(q),
         _stream(stream)))
 
 

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "pkv_internal.h"
 
@@ -355,6 +356,16 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
 
 }  // extern "C"
 
+// ---- Library-owned decode scratch for callers that cannot allocate ----
+// One statically sized device array per GPU the library runs on (each device holds its own copy
+// at its own address until the process ends). It takes the place of the caller's workspace:
+// split-stream partials from its start, arrival counters in its last 4 bytes per workgroup. In
+// host code `scratch` is only a stand-in for the symbol; its device address on the current device
+// comes from hipGetSymbolAddress and is the only form passed to kernels.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+static_assert(PKV_NOALLOC_SCRATCH_BYTES % 256 == 0, "the scratch size is a whole number of lines");
+
 namespace {
 
 // Decode, plain or fused with the append of each sequence's newest token (new_k / new_v non-null:
@@ -434,9 +445,72 @@ pkv_status decode_impl(void* out, const void* q, const void* new_k, const void* 
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+constexpr int kMaxDevices = 64;
+constexpr int kScratchCounterWords = 4096;  // counters cleared at set-up: more than any grid uses
+
+__global__ void clear_words_kernel(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Device address of the scratch array on the current device. The first call on a device looks it
+// up and clears the counter words with a fill kernel on `stream` (a kernel, so that the clear is
+// also valid inside a stream being captured into a graph); later calls rely on every completed
+// decode leaving its counters zero.
+pkv_status scratch_address(hipStream_t stream, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return PKV_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return PKV_ERR_HIP;
+    }
+    unsigned* counters = (unsigned*)((char*)p + PKV_NOALLOC_SCRATCH_BYTES) - kScratchCounterWords;
+    hipLaunchKernelGGL(clear_words_kernel, dim3((kScratchCounterWords + 255) / 256), dim3(256), 0,
+                       stream, counters, kScratchCounterWords);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+pkv_status paged_attention_decode_noalloc(void* out, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_tables,
+                                          const int32_t* context_lens, float scale,
+                                          int num_q_heads, int num_kv_heads, int head_dim,
+                                          int block_size, int num_seqs, int max_blocks_per_seq,
+                                          int max_context_len, int num_workgroups,
+                                          pkv_dtype dtype, hipStream_t stream) {
+  if (!decode_shape_ok(num_seqs, num_q_heads, num_kv_heads, max_context_len, block_size,
+                       num_workgroups))
+    return PKV_ERR_INVALID_ARG;
+  if (!supported_shape(head_dim, block_size, dtype)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  const int grid = resolve_workgroups(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                                      num_workgroups);
+  if (workspace_bytes_for(grid, head_dim) > PKV_NOALLOC_SCRATCH_BYTES ||
+      grid > kScratchCounterWords)
+    return PKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const pkv_status st = scratch_address(stream, &ws);
+  if (st != PKV_OK) return st;
+  return decode_impl(out, q, nullptr, nullptr, k_pool, v_pool, block_tables, context_lens, scale,
+                     false, 1.0f, 1.0f, num_q_heads, num_kv_heads, head_dim, block_size, num_seqs,
+                     max_blocks_per_seq, max_context_len, num_workgroups, dtype, ws,
+                     PKV_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 pkv_status paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_tables, const int32_t* context_lens,
