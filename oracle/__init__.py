@@ -69,6 +69,8 @@ def _load():
     lib.oracle_reshape_and_cache8.restype = i
     lib.oracle_dead_slot_indices.argtypes = [i, i, p, p, i, i, i, i, i, p, lg]
     lib.oracle_dead_slot_indices.restype = lg
+    lib.oracle_slot_indices.argtypes = [i, i, p, i, i, i, i, p, lg]
+    lib.oracle_slot_indices.restype = lg
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i
     _lib = lib
@@ -124,6 +126,22 @@ def dead_slot_indices(is_v: bool, fp8: bool, block_tables, context_lens, num_kv_
     n = int(_load().oracle_dead_slot_indices(*args, None, 0))
     out = np.zeros(max(n, 1), np.int64)
     _load().oracle_dead_slot_indices(*args, _ptr(out), n)
+    return out[:n]
+
+
+def slot_indices(is_v: bool, fp8: bool, slot_mapping, num_kv_heads: int, block_size: int,
+                 head_dim: int) -> np.ndarray:
+    """int64 pool indices (pool_index / pool_index8) of the whole token rows named by the
+    non-negative slots (all kv heads and dims)."""
+    sm = slot_mapping
+    if not isinstance(sm, np.ndarray):
+        sm = sm.contiguous().numpy()
+    sm = np.ascontiguousarray(sm, dtype=np.int64)
+    args = (int(bool(is_v)), int(bool(fp8)), _ptr(sm), sm.shape[0], num_kv_heads, block_size,
+            head_dim)
+    n = int(_load().oracle_slot_indices(*args, None, 0))
+    out = np.zeros(max(n, 1), np.int64)
+    _load().oracle_slot_indices(*args, _ptr(out), n)
     return out[:n]
 
 

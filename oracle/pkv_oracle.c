@@ -423,6 +423,29 @@ long oracle_dead_slot_indices(int is_v, int fp8, const int32_t* block_tables,
   return k;
 }
 
+/*
+ * Pool indices of whole token rows: for each slot of slots[0..n) that is >= 0 (slot = block * B
+ * + t, the form reshape_and_cache takes), every kv head and dim, in that order. fp8 selects
+ * pool_index8. Writes at most cap indices to out (out may be NULL); returns how many there are.
+ */
+long oracle_slot_indices(int is_v, int fp8, const int64_t* slots, int n, int Hkv, int B, int D,
+                         long* out, long cap) {
+  long k = 0;
+  for (int i = 0; i < n; ++i) {
+    if (slots[i] < 0) continue;
+    long b = (long)(slots[i] / B);
+    int t = (int)(slots[i] % B);
+    for (int h = 0; h < Hkv; ++h)
+      for (int d = 0; d < D; ++d) {
+        if (out != NULL && k < cap)
+          out[k] = (long)(fp8 ? pool_index8(is_v, b, h, t, d, Hkv, B, D)
+                              : pool_index(is_v, b, h, t, d, Hkv, B, D));
+        ++k;
+      }
+  }
+  return k;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -1,11 +1,9 @@
 """CPU-only checks of the Python binding's argument validation: every malformed tensor is refused
 with ValueError before anything reaches the library (no GPU involved: the refusals come before
 the device check, so host tensors exercise them)."""
-import numpy as np
 import pytest
 import torch
 
-import oracle
 import paged_kv_cache_452_amd as pkv
 
 S, HQ, HKV, D, B = 3, 8, 2, 64, 16
@@ -112,20 +110,3 @@ def test_reshape_refuses_malformed_arguments(fp8):
 def test_copy_blocks_refuses_int64_ids():
     with pytest.raises(ValueError, match="src_blocks: element type"):
         pkv.copy_blocks(None, torch.zeros(4, dtype=torch.int64), torch.zeros(4, dtype=torch.int32))
-
-
-@pytest.mark.parametrize("fp8", [False, True])
-def test_dead_slot_indices_equal_the_per_element_enumeration(fp8):
-    """The oracle's vectorised dead-slot list (used to NaN-poison unused slots) is exactly the
-    slots t >= n mod B of each partly filled last block, located by pool_index / pool_index8."""
-    Hkv, Bs, Dd = 3, 32, 64
-    lens = np.array([0, 1, 31, 32, 33, 70], np.int32)
-    rng = np.random.default_rng(3)
-    bt = rng.permutation(40)[:6 * 3].reshape(6, 3).astype(np.int32)
-    index = oracle.pool_index8 if fp8 else oracle.pool_index
-    for is_v in (False, True):
-        want = [index(is_v, int(bt[s][n // Bs]), h, t, d, Hkv, Bs, Dd)
-                for s, n in enumerate(lens) if n % Bs
-                for t in range(n % Bs, Bs) for h in range(Hkv) for d in range(Dd)]
-        got = oracle.dead_slot_indices(is_v, fp8, bt, lens, Hkv, Bs, Dd)
-        assert got.tolist() == want

@@ -173,27 +173,41 @@ def test_fp8_step_reshape_then_decode():
     assert_close(out, ref, "fp8 step")
 
 
-def test_fp8_70b_shaped_step_every_layer_and_row():
-    """The benchmark's fp8 step on the 70B-shaped batch, checked in full: for each of the 80
-    layers, reshape_and_cache_fp8 of the 64 new tokens (the whole layer's K and V planes equal the
-    oracle's quantizing scatter byte for byte), then decode over the E4M3 pools (every (sequence,
-    head) row against the oracle)."""
+LAYER_CHUNK = 10   # layers per test of the full-size check (each test stays well under a minute)
+
+
+@pytest.fixture(scope="module")
+def batch70_fp8():
+    """The 70B-shaped batch over fp8 pools (80 layers, 2 x 20 GiB), built once for this module."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
     spec = workloads.SPECS[4]
     t = workloads.make_tables(spec)
     say("fp8 pools, 70B-shaped batch: allocating and filling 2 x 20 GiB")
     b = workloads.make_batch_fp8(spec, device=DEV, tables=t)
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
-    ks, vs = 0.5, 0.5
     ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, 4096), DEV)
+    yield spec, t, b, LayerHost(b.kv_pool[0]), ws
+    del b, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("first", range(0, 80, LAYER_CHUNK))
+def test_fp8_70b_shaped_step_every_layer_and_row(batch70_fp8, first):
+    """The benchmark's fp8 step on the 70B-shaped batch, checked in full (10 layers per test):
+    for each layer, reshape_and_cache_fp8 of the 64 new tokens (the whole layer's K and V planes
+    equal the oracle's quantizing scatter byte for byte), then decode over the E4M3 pools (every
+    (sequence, head) row against the oracle)."""
+    spec, t, b, host, ws = batch70_fp8
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    ks, vs = 0.5, 0.5
     out = torch.empty_like(b.q)
-    host = LayerHost(b.kv_pool[0])
     key, value = b.new_key.cpu(), b.new_value.cpu()
-    for L in range(spec.num_layers):
+    for L in range(first, first + LAYER_CHUNK):
         kb, vb = host.planes(b.kv_pool[L])
         oracle.reshape_and_cache8(kb, vb, key, value, oracle.BF16, ks, vs, t.slot_mapping, Hkv,
                                   D, 16, t.num_blocks)
-        if L % 10 == 0:
-            say("fp8 step, 70B-shaped batch, layer", L)
+        say("fp8 step, 70B-shaped batch, layer", L)
         pkv.reshape_and_cache_fp8(b.new_key, b.new_value, b.k_pool[L], b.v_pool[L],
                                   b.slot_mapping, t.num_blocks, ks, vs)
         pkv.paged_attention_decode_fp8(out, b.q, b.k_pool[L], b.v_pool[L], b.block_tables,
@@ -204,8 +218,6 @@ def test_fp8_70b_shaped_step_every_layer_and_row():
         ref = oracle_decode8(b.q, kb, vb, t.block_tables, t.context_lens, spec.scale, ks, vs, Hq,
                              Hkv, t.num_blocks)
         assert_close(out, ref, f"fp8 layer {L}")
-    del b, host
-    torch.cuda.empty_cache()
 
 
 def test_copy_blocks_fp8_pool_bit_exact():

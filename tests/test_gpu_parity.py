@@ -86,26 +86,40 @@ def test_tiny_batch_two_steps_cross_block_boundary():
     assert_close(out2, ref2, "step 2")
 
 
-def test_70b_shaped_step_every_layer_and_row():
-    """The benchmark's workload and step, checked in full: the 70B-shaped batch (64 x 4096 tokens,
-    64/8 heads, d128, bf16) in one 80 GiB pool; for every one of the 80 layers, reshape_and_cache
-    of the 64 new tokens (the whole layer's K and V planes equal the oracle's scatter word for
-    word) then decode (every (sequence, head) row against the oracle)."""
+LAYER_CHUNK = 10   # layers per test of the full-size checks (each test stays well under a minute)
+
+
+@pytest.fixture(scope="module")
+def batch70():
+    """The 70B-shaped batch (64 x 4096 tokens, 64/8 heads, d128, bf16, 80 layers in one 80 GiB
+    pool), built once for the full-size checks of this module."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
     spec = workloads.SPECS[4]
     t = workloads.make_tables(spec)
     say("70B-shaped batch: allocating and filling 2 x 40 GiB")
     batch = workloads.make_batch(spec, device=DEV, tables=t)
     S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, 4096), DEV)
+    yield spec, t, batch, LayerHost(batch.kv_pool[0]), ws
+    del batch, ws
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("first", range(0, 80, LAYER_CHUNK))
+def test_70b_shaped_step_every_layer_and_row(batch70, first):
+    """The benchmark's workload and step, checked in full (10 layers per test, all 80 over the
+    set): for each layer, reshape_and_cache of the 64 new tokens (the whole layer's K and V planes
+    equal the oracle's scatter word for word) then decode (every (sequence, head) row against the
+    oracle)."""
+    spec, t, batch, host, ws = batch70
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     out = torch.empty_like(batch.q)
-    host = LayerHost(batch.kv_pool[0])
     key, value = batch.new_key.cpu(), batch.new_value.cpu()
-    worst = (0.0, 0.0)
-    for L in range(spec.num_layers):
+    for L in range(first, first + LAYER_CHUNK):
         kw, vw = host.planes(batch.kv_pool[L])
         oracle.reshape_and_cache(kw, vw, key, value, t.slot_mapping, Hkv, D, 16, t.num_blocks)
-        if L % 10 == 0:
-            say("70B-shaped step, layer", L)
+        say("70B-shaped step, layer", L)
         k, v = _layer(batch, L)
         pkv.reshape_and_cache(batch.new_key, batch.new_value, k, v, batch.slot_mapping,
                               t.num_blocks)
@@ -115,11 +129,32 @@ def test_70b_shaped_step_every_layer_and_row():
         assert host.equals(batch.kv_pool[L], kw, vw), f"layer {L}: pool differs after reshape"
         ref = oracle_decode(batch.q, None, None, t.block_tables, t.context_lens, spec.scale, Hq,
                             Hkv, t.num_blocks, k_words=kw, v_words=vw)
-        e = assert_close(out, ref, f"layer {L}")
-        worst = (max(worst[0], e[0]), max(worst[1], e[1]))
-    say("70B-shaped step: worst max_abs %.3e rel_l2 %.3e over 80 layers" % worst)
-    del batch, host
-    torch.cuda.empty_cache()
+        assert_close(out, ref, f"layer {L}")
+
+
+@pytest.mark.parametrize("first", range(0, 80, LAYER_CHUNK))
+def test_fused_append_70b_shaped_every_layer_and_row(batch70, first):
+    """The fused step on the 70B-shaped batch, checked in full (10 layers per test): the new
+    tokens' slots are NaN before each launch; after it, the layer's K and V planes equal the
+    oracle's scatter word for word and every (sequence, head) row matches the oracle."""
+    spec, t, batch, host, ws = batch70
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    out = torch.empty_like(batch.q)
+    key, value = batch.new_key.cpu(), batch.new_value.cpu()
+    for L in range(first, first + LAYER_CHUNK):
+        _poison_new_slots_(batch.k_pool[L], batch.v_pool[L], t, Hkv, D, 16)
+        kw, vw = host.planes(batch.kv_pool[L])
+        oracle.reshape_and_cache(kw, vw, key, value, t.slot_mapping, Hkv, D, 16, t.num_blocks)
+        say("fused step, 70B-shaped batch, layer", L)
+        pkv.paged_attention_decode_append(out, batch.q, batch.new_key, batch.new_value,
+                                          batch.k_pool[L], batch.v_pool[L], batch.block_tables,
+                                          batch.context_lens, spec.scale, Hq, Hkv, D, 16, 4096, 0,
+                                          ws)
+        torch.cuda.synchronize()
+        assert host.equals(batch.kv_pool[L], kw, vw), f"layer {L}: pool differs"
+        ref = oracle_decode(batch.q, None, None, t.block_tables, t.context_lens, spec.scale, Hq,
+                            Hkv, t.num_blocks, k_words=kw, v_words=vw)
+        assert_close(out, ref, f"fused layer {L}")
 
 
 def _random_case(Hq, Hkv, D, lens, dtype=torch.bfloat16, seed=0, extra_blocks=7, block_size=16):
@@ -277,22 +312,19 @@ def test_reshape_and_cache_skips_negative_and_past_pool_slots():
 
 # ---- One fused step: paged_attention_decode_append = reshape_and_cache + decode ----
 
+def _new_slots(t, B):
+    """Slot of each sequence's newest token (position n - 1), -1 for empty sequences."""
+    return np.array([int(t.block_tables[s][(int(n) - 1) // B]) * B + (int(n) - 1) % B if n > 0
+                     else -1 for s, n in enumerate(t.context_lens)], np.int64)
+
+
 def _poison_new_slots_(k, v, t, Hkv, D, B):
     """NaN into the slot each sequence's new token goes to: the fused launch must write the token
     there before it reads the slot's tile, or the NaN reaches the output."""
-    idx = []
-    for s, n in enumerate(t.context_lens):
-        n = int(n)
-        if n == 0:
-            continue
-        b = int(t.block_tables[s][(n - 1) // B])
-        for h in range(Hkv):
-            for d in range(D):
-                idx.append((oracle.pool_index(False, b, h, (n - 1) % B, d, Hkv, B, D),
-                            oracle.pool_index(True, b, h, (n - 1) % B, d, Hkv, B, D)))
-    ia = torch.tensor(idx, dtype=torch.long, device=k.device)
-    set_plane_(k, ia[:, 0], float("nan"))
-    set_plane_(v, ia[:, 1], float("nan"))
+    slots = _new_slots(t, B)
+    for plane, is_v in ((k, False), (v, True)):
+        idx = oracle.slot_indices(is_v, False, slots, Hkv, B, D)
+        set_plane_(plane, torch.from_numpy(idx).to(plane.device), float("nan"))
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,dtype,lens,B,nwg", [
@@ -331,37 +363,6 @@ def test_fused_append_decode_matches_oracle(Hq, Hkv, D, dtype, lens, B, nwg):
         if n == 1:   # softmax over one token: the output is its value row, exactly
             g = torch.arange(Hq, device=DEV) // (Hq // Hkv)
             assert torch.equal(out[s].view(torch.int16), b.new_value[s][g].view(torch.int16))
-
-
-def test_fused_append_70b_shaped_every_layer_and_row():
-    """The fused step on the 70B-shaped batch, checked in full: every layer appends and decodes in
-    one launch; each layer's K and V planes equal the oracle's scatter word for word and every
-    (sequence, head) row matches the oracle."""
-    spec = workloads.SPECS[4]
-    t = workloads.make_tables(spec)
-    say("fused step, 70B-shaped batch: allocating and filling 2 x 40 GiB")
-    batch = workloads.make_batch(spec, device=DEV, tables=t)
-    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
-    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, 16, 4096), DEV)
-    out = torch.empty_like(batch.q)
-    host = LayerHost(batch.kv_pool[0])
-    key, value = batch.new_key.cpu(), batch.new_value.cpu()
-    for L in range(spec.num_layers):
-        kw, vw = host.planes(batch.kv_pool[L])
-        oracle.reshape_and_cache(kw, vw, key, value, t.slot_mapping, Hkv, D, 16, t.num_blocks)
-        if L % 10 == 0:
-            say("fused step, 70B-shaped batch, layer", L)
-        pkv.paged_attention_decode_append(out, batch.q, batch.new_key, batch.new_value,
-                                          batch.k_pool[L], batch.v_pool[L], batch.block_tables,
-                                          batch.context_lens, spec.scale, Hq, Hkv, D, 16, 4096, 0,
-                                          ws)
-        torch.cuda.synchronize()
-        assert host.equals(batch.kv_pool[L], kw, vw), f"layer {L}: pool differs"
-        ref = oracle_decode(batch.q, None, None, t.block_tables, t.context_lens, spec.scale, Hq,
-                            Hkv, t.num_blocks, k_words=kw, v_words=vw)
-        assert_close(out, ref, f"fused layer {L}")
-    del batch, host
-    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("table,n", [
