@@ -1,17 +1,18 @@
 // Paged-attention decode kernel for gfx950 (MI355X).
 //
 // Work decomposition. Every (sequence s, kv head g, tile of <= 16 query heads) is one *stream* of
-// nb_s = ceil(n_s / 16) blocks. The streams are laid end to end, sequence-major, into one
-// flattened space of W = sum_s nb_s * (kv heads * head tiles) block positions, and the launch's
-// workgroups cut that space into contiguous ranges: equal ones, or (when the equal cut would split
-// streams anyway) ranges weighted by the XCD a workgroup runs on, since odd-numbered XCDs stream
-// measurably slower (see range_start). When the library chose the full grid and the batch has no
-// more streams than workgroups, of uneven lengths, only the first half of the workgroups (one
-// per compute unit) take ranges, which halves the streams the cut splits. A workgroup's share is
-// thus fixed whatever the mix of
-// context lengths: a 32k-token sequence is spread over many workgroups and a batch of short ones
-// is packed into few, with no per-sequence partition size to tune and no tail of idle compute
-// units. Each workgroup derives the plan itself from context_lens (a prefix sum in LDS), so the
+// nb_s = ceil(n_s / 16) blocks. The streams are laid end to end, (kv head, head tile)-major and
+// then by sequence, into one flattened space of W = sum_s nb_s * (kv heads * head tiles) block
+// positions, and the launch's workgroups cut that space into contiguous ranges: equal ones, or
+// (when the equal cut would split streams anyway) ranges weighted by the XCD a workgroup runs on,
+// since odd-numbered XCDs stream measurably slower (see range_start). Consecutive ranges run on
+// one XCD (range_of_workgroup), so the sequences of one kv head -- and the blocks they share, such
+// as a common prompt prefix -- are read through one L2. When the library chose the full grid and
+// the batch has no more streams than workgroups, of uneven lengths, only the first half of the
+// workgroups (one per compute unit) take ranges, which halves the streams the cut splits. A
+// workgroup's share is thus fixed whatever the mix of context lengths: a 32k-token sequence is
+// spread over many workgroups and a batch of short ones is packed into few, with no per-sequence
+// partition size to tune and no tail of idle compute units. Each workgroup derives the plan itself from context_lens (a prefix sum in LDS), so the
 // host needs no device data.
 //
 // Inside a range the four wavefronts interleave block by block (wave i takes positions
@@ -256,7 +257,12 @@ paged_decode_kernel(DecodeLaunch a) {
   }
 
   const int Hh = a.num_kv_heads * a.head_tiles;  // streams per sequence
-  const int W = uniform(Hh * s_ps[S]);
+  // Flattened order: (kv head, head tile) gh major, then sequence, then 16-token unit. Stream
+  // (s, gh) holds positions [gh T + s_ps[s], gh T + s_ps[s + 1]), so the sequences that share
+  // one kv head's blocks are neighbours in the order (and, through the XCD blocks of the ranges,
+  // read on one XCD).
+  const int T = uniform(s_ps[S]);  // units of one (kv head, head tile) over all sequences
+  const int W = Hh * T;
   int nwg = min((int)gridDim.x, W);
   if (nwg == 0) return;  // no positions at all (every sequence empty): uniform over the launch
   // Weighted ranges only when they can help and cannot hurt:
@@ -281,21 +287,23 @@ paged_decode_kernel(DecodeLaunch a) {
     nwg /= 2;
     aligned = aligned_for(nwg);
   }
-  const int wg = blockIdx.x;
-  if (wg >= nwg) return;  // uniform over the workgroup
+  if ((int)blockIdx.x >= nwg) return;  // uniform over the workgroup
+  const int wg = range_of_workgroup(blockIdx.x, nwg);  // this workgroup's range
   const int odd_w = W >= 2 * nwg && !aligned ? a.odd_weight : kEvenWeight;
   const int r0 = range_start(wg, nwg, W, odd_w);
   const int r1 = range_start(wg + 1, nwg, W, odd_w);
 
-  // Sequence whose streams hold flattened position p: the last s with Hh * s_ps[s] <= p.
-  auto seq_of = [&](int p) {
-    const int x = p / Hh;
+  // The stream holding flattened position p: gh = p / T, and the sequence s is the last one with
+  // s_ps[s] <= p - gh T (empty sequences before it share its s_ps).
+  auto locate = [&](int p, int& s, int& gh) {
+    gh = p / T;
+    const int x = p - gh * T;
     int lo = 0, hi = S;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_ps[mid] <= x) lo = mid; else hi = mid;
     }
-    return lo;
+    s = lo;
   };
 
   // ---- Streams (uniform cursor). ----
@@ -313,7 +321,7 @@ paged_decode_kernel(DecodeLaunch a) {
       const int pb = uniform(s_ps[s]);
       const int nb = uniform(s_ps[s + 1]) - pb;
       t.n = uniform(s_len[s]);
-      t.start = Hh * pb + gh * nb;
+      t.start = gh * T + pb;
       t.end = t.start + nb;
       const int g = gh / a.head_tiles;
       const int ht = gh - g * a.head_tiles;
@@ -327,23 +335,26 @@ paged_decode_kernel(DecodeLaunch a) {
     }
     return t;
   };
+  auto first_nonempty = [&](int s) {
+    while (s < S && uniform(s_ps[s + 1]) == uniform(s_ps[s])) ++s;  // skip empty sequences
+    return s;
+  };
   auto stream_after = [&](const Stream& c) {
-    int gh = c.gh + 1, s = c.s;
-    if (gh == Hh) {
-      gh = 0;
-      ++s;
-      while (s < S && uniform(s_ps[s + 1]) == uniform(s_ps[s])) ++s;  // skip empty sequences
+    int s = first_nonempty(c.s + 1), gh = c.gh;
+    if (s == S) {  // the next (kv head, head tile): its first non-empty sequence
+      ++gh;
+      s = gh < Hh ? first_nonempty(0) : S;
     }
     return stream_at(s, gh);
   };
+  // The stream starting at (or holding) flattened position p.
+  auto stream_from = [&](int p) {
+    int s, gh;
+    locate(p, s, gh);
+    return stream_at(uniform(s), uniform(gh));
+  };
 
-  Stream cur;
-  {
-    const int s0 = uniform(seq_of(r0));
-    const int pb = uniform(s_ps[s0]);
-    const int nb = uniform(s_ps[s0 + 1]) - pb;
-    cur = stream_at(s0, (r0 - Hh * pb) / nb);
-  }
+  Stream cur = stream_from(r0);
 
   // ---- q: the head rows of the range's first streams, staged in LDS for all four waves. The
   // loads go out here; the rows are stored into LDS after the tile-id loads below have gone out
@@ -396,12 +407,9 @@ paged_decode_kernel(DecodeLaunch a) {
       j = p - cur.start;
       g = cur.gh / a.head_tiles;
     } else {
-      s = seq_of(p);
-      const int pb = s_ps[s];
-      const int nb = s_ps[s + 1] - pb;
-      const int r = p - Hh * pb;
-      const int gh = r / nb;
-      j = r - gh * nb;
+      int gh;
+      locate(p, s, gh);
+      j = p - gh * T - s_ps[s];
       g = gh / a.head_tiles;
     }
     // 16-token unit j of the stream: sub-tile j % R of physical block block_tables[s][j / R]
@@ -853,13 +861,6 @@ paged_decode_kernel(DecodeLaunch a) {
   // Split 0 was counted when its stream ended (s_last[0]); split 1 is counted here.
   const bool has0 = split0 >= 0, has1 = split1 >= 0;
   if (has0 || has1) {
-    // The stream starting at flattened position p.
-    auto stream_from = [&](int p) {
-      const int s = uniform(seq_of(p));
-      const int pb = uniform(s_ps[s]);
-      const int nb = uniform(s_ps[s + 1]) - pb;
-      return stream_at(s, (p - Hh * pb) / nb);
-    };
     const Stream st0 = stream_from(has0 ? split0 : split1);
     const Stream st1 = stream_from(has1 ? split1 : split0);
     const int np1 = range_owner(st1.end - 1, nwg, W, odd_w) - wg + 1;  // st1 starts in this range

@@ -50,37 +50,60 @@ __device__ __forceinline__ unsigned e4m3_code(float y) {
 }
 
 // ---- Decode workgroup ranges ----
-// Workgroups are dispatched round-robin over the 8 XCDs (XCD = blockIdx % 8), and on MI355X the
-// odd-numbered XCDs stream measurably slower (about 9% on the 70B-shaped decode, on every board
-// measured). Each workgroup's share of the flattened positions is therefore proportional to a
-// weight: kEvenWeight on even XCDs, odd_weight on odd ones, so that all finish together.
-// Workgroup w covers [range_start(w), range_start(w + 1)).
+// The decode cuts its flattened block positions [0, W) into nwg contiguous ranges, one per
+// workgroup. Workgroups are dispatched round-robin over the 8 XCDs of MI355X (XCD = blockIdx % 8
+// when the GPU runs as one partition, SPX), each XCD with its own L2. When nwg is a multiple of
+// 8 the ranges are handed out in XCD blocks: range r runs on workgroup (r % P) * 8 + r / P,
+// P = nwg / 8, so XCD x executes the P consecutive ranges [x P, (x + 1) P) -- one contiguous
+// stretch of positions, and streams that read the same blocks (a shared prompt prefix) are read
+// through one L2. Otherwise range r runs on workgroup r.
+// The odd-numbered XCDs stream measurably slower (about 9% on the 70B-shaped decode, on every
+// board measured), so a range's share is proportional to a weight: kEvenWeight for ranges of an
+// even XCD block, odd_weight for an odd one (with one block, every range weighs kEvenWeight).
+// Range r covers [range_start(r), range_start(r + 1)).
 constexpr int kEvenWeight = 1024;
 
-// C(w): sum of the weights of workgroups 0 .. w - 1.
-__host__ __device__ inline long long range_cum_weight(int w, int odd_weight) {
-  const int r = w & 7;
-  return (long long)(w >> 3) * (4LL * kEvenWeight + 4LL * odd_weight) +
-         (long long)((r + 1) / 2) * kEvenWeight + (long long)(r / 2) * odd_weight;
+// XCD blocks the ranges of an nwg-workgroup launch are grouped in: 8, or 1 (no grouping).
+__host__ __device__ inline int range_blocks(int nwg) { return nwg % 8 == 0 ? 8 : 1; }
+
+// The range workgroup w executes, and its inverse.
+__host__ __device__ inline int range_of_workgroup(int w, int nwg) {
+  const int nx = range_blocks(nwg), per = nwg / nx;
+  return (w % nx) * per + w / nx;
+}
+__host__ __device__ inline int workgroup_of_range(int r, int nwg) {
+  const int nx = range_blocks(nwg), per = nwg / nx;
+  return (r % per) * nx + r / per;
 }
 
-__host__ __device__ inline int range_start(int w, int nwg, int W, int odd_weight) {
-  return (int)((long long)W * range_cum_weight(w, odd_weight) /
-               range_cum_weight(nwg, odd_weight));
+// C(r): sum of the weights of ranges 0 .. r - 1 (r in [0, nwg]).
+__host__ __device__ inline long long range_cum_weight(int r, int nwg, int odd_weight) {
+  const int nx = range_blocks(nwg), per = nwg / nx;
+  const int x = r / per;
+  const int i = r - x * per;
+  const long long w = nx == 1 ? kEvenWeight : (x & 1) ? odd_weight : kEvenWeight;
+  const long long ow = nx == 1 ? kEvenWeight : odd_weight;
+  return (long long)per * ((long long)((x + 1) / 2) * kEvenWeight + (long long)(x / 2) * ow) +
+         (long long)i * w;
 }
 
-// The workgroup whose range holds position p (0 <= p < W): the last w < nwg with
-// range_start(w) <= p, i.e. with C(w) <= ceil((p + 1) C(nwg) / W) - 1.
+__host__ __device__ inline int range_start(int r, int nwg, int W, int odd_weight) {
+  return (int)((long long)W * range_cum_weight(r, nwg, odd_weight) /
+               range_cum_weight(nwg, nwg, odd_weight));
+}
+
+// The range holding position p (0 <= p < W): the last r < nwg with range_start(r) <= p, i.e. with
+// C(r) <= ceil((p + 1) C(nwg) / W) - 1: first the XCD block, then the range inside it.
 __host__ __device__ inline int range_owner(int p, int nwg, int W, int odd_weight) {
-  const long long x = ((long long)(p + 1) * range_cum_weight(nwg, odd_weight) - 1) / W;
-  const long long period = 4LL * kEvenWeight + 4LL * odd_weight;
-  const long long q = x / period;
-  const long long rem = x - q * period;
-  int r = 7;
-  while (r > 0 && (long long)((r + 1) / 2) * kEvenWeight + (long long)(r / 2) * odd_weight > rem)
-    --r;
-  const long long w = q * 8 + r;
-  return (int)(w < nwg - 1 ? w : nwg - 1);
+  const long long x = ((long long)(p + 1) * range_cum_weight(nwg, nwg, odd_weight) - 1) / W;
+  const int nx = range_blocks(nwg), per = nwg / nx;
+  int b = nx - 1;
+  while (b > 0 && range_cum_weight(b * per, nwg, odd_weight) > x) --b;
+  const long long w = nx == 1 ? kEvenWeight : (b & 1) ? odd_weight : kEvenWeight;
+  long long i = (x - range_cum_weight(b * per, nwg, odd_weight)) / w;
+  if (i > per - 1) i = per - 1;
+  const long long r = (long long)b * per + i;
+  return (int)(r < nwg - 1 ? r : nwg - 1);
 }
 
 struct DecodeLaunch {
