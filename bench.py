@@ -2,9 +2,11 @@
 
 Default workload: the Llama-3-70B-shaped batch (64 sequences x 4096 tokens, 64 query / 8 kv
 heads, head dim 128, bf16, 80 layers in one 80 GiB K+V pool, 16384 blocks per layer scattered by
-a seeded permutation). Prints one JSON line.
+a seeded permutation). The default run also measures the Llama-3-8B-shaped ragged batch (8 layers)
+as "secondary", and the CPU oracle as "cpu_baseline". Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--layers L] [--no-cpu-baseline]
+                  [--no-secondary]
 """
 from __future__ import annotations
 
@@ -87,8 +89,9 @@ def source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel code (comments aside) and this workload."""
+    """L2-to-fabric bytes per decode launch (reads and writes) from the committed rocprofv3
+    counter summary, if it was taken on the current kernel code (comments aside) and this
+    workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             recs = json.load(f).get("records", [])
@@ -164,7 +167,7 @@ def cpu_baseline(batch, spec, layers, budget_s=15.0, kv_scales=None):
                             t.num_blocks, qdt, pairs=pairs, threads=1)
     one_s = time.perf_counter() - t0
     return {"value": round(done_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n_layers} whole layer(s) of the same batch ({spec.num_seqs} seqs x "
                       f"{spec.num_q_heads} heads each), fp64, timed from host-resident pools; "
                       f"device-to-host copy {d2h_s:.2f} s not included",
@@ -172,6 +175,64 @@ def cpu_baseline(batch, spec, layers, budget_s=15.0, kv_scales=None):
             "single_thread": {"value": round(one_bytes / one_s / 1e9, 4), "unit": "GB/s",
                               "cores": 1, "sample": f"every head of the first {n_seq} "
                               f"sequence(s) of one layer", "seconds": round(one_s, 3)}}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def single_thread_rates(min_bytes: float = 100e6):
+    """The oracle on one host thread over the tiny, 13B-shaped and 8B-shaped batches (one layer
+    each, built on the GPU and copied to the host): the whole tiny batch (repeated for at least
+    0.2 s), and every head of the first sequences of the others until about 100 MB of K/V."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+
+    rates = {}
+    for idx in (1, 2, 3):
+        spec = workloads.SPECS[idx]
+        t = workloads.make_tables(spec)
+        b = workloads.make_batch(spec, device="cuda", tables=t)
+        h = b.kv_pool[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        kw, vw = np.ascontiguousarray(h[:, :, 0, :]), np.ascontiguousarray(h[:, :, 1, :])
+        q = b.q.cpu()
+        del b
+        lens = np.asarray(t.context_lens)
+        qdt = oracle.BF16 if spec.dtype == "bf16" else oracle.FP16
+        n_seq = 1
+        while n_seq < len(lens) and algorithmic_bytes(
+                lens[:n_seq], spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                block=spec.block_size) < min_bytes:
+            n_seq += 1
+        pairs = [(s, hh) for s in range(n_seq) for hh in range(spec.num_q_heads)]
+        nbytes = algorithmic_bytes(lens[:n_seq], spec.num_q_heads, spec.num_kv_heads,
+                                   spec.head_dim, block=spec.block_size)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.paged_decode(q, kw, vw, t.block_tables, t.context_lens, spec.scale,
+                                spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                                spec.block_size, t.num_blocks, qdt, pairs=pairs, threads=1)
+            reps += 1
+            if time.perf_counter() - t0 >= 0.2:
+                break
+        sec = (time.perf_counter() - t0) / reps
+        rates[SPEC_NAMES[idx]] = {
+            "value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "sample": (f"every head of the first {n_seq} of {len(lens)} sequences of one layer "
+                       f"({nbytes / 1e6:.1f} MB of algorithmic bytes)"),
+            "seconds_per_sample": round(sec, 4)}
+        torch.cuda.empty_cache()
+    return rates
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 3) -> int:
@@ -354,6 +415,8 @@ def main() -> int:
                     help="run each layer's step as one paged_attention_decode_append launch "
                          "instead of reshape_and_cache followed by paged_attention_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the 8B-shaped batch measured after the default 70B-shaped one")
     ap.add_argument("--kernel", choices=["decode", "copy_blocks", "swap"], default="decode",
                     help="decode (the hot path, default), copy_blocks (copy-on-write copies) or "
                          "swap (preemption to and from pinned host memory)")
@@ -376,16 +439,99 @@ def main() -> int:
     if args.kernel == "swap":
         return bench_swap(args)
     pkv.load_library()
-    dev = "cuda"
     spec = workloads.SPECS[args.config]
     if args.layers > 0:
         spec = dataclasses.replace(spec, num_layers=args.layers)
     if args.block_size != spec.block_size:
         spec = dataclasses.replace(spec, block_size=args.block_size)
+    fp8 = args.kv_dtype == "fp8"
+    m = measure_decode(spec, args.steps, args.warmup, args.workgroups, fp8, args.fused,
+                       named_layers=args.layers > 0)
+    t, L, S = m["tables"], spec.num_layers, spec.num_seqs
+    Hq, Hkv, D, B = spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.block_size
+    rec = {
+        "metric": METRIC,
+        "value": round(m["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": m["workload"], "num_seqs": S, "context_lens": "all 4096" if
+                   args.config == 4 else "seeded", "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": B, "num_layers": L,
+                   "num_blocks_per_layer": t.num_blocks, "decode_workgroups": m["grid"],
+                   "kv_dtype": "fp8 e4m3, one scale per pool" if fp8 else spec.dtype,
+                   "step": ("per layer: reshape_and_cache of the step's new tokens, then "
+                            "paged_attention_decode" if not args.fused else
+                            "per layer: one paged_attention_decode_append launch (the step's new "
+                            "tokens appended to the pool and attended to with the cached "
+                            "context)")},
+        "pct_of_hbm_peak": round(100.0 * m["value"] / HBM_PEAK_GBS, 2),
+        "tokens_per_s_per_layer_step": round(S * L / (m["ms_step"] * 1e-3), 1),
+        "decode_launch_us": round(m["decode_us"], 2),
+        "decode_launch_us_spread": m["spread"],
+        "timing": "roofline.achieved: back-to-back step launches of the decode kernel over all "
+                  "layers between two HIP events on the launch stream (mean launch duration), "
+                  "timed first; value: K whole steps between two HIP events",
+        "roofline": m["roofline"],
+    }
+    if "unique_kv" in m:
+        rec["unique_kv"] = m["unique_kv"]
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    rec["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "compute_units": props.multi_processor_count, "hip": torch.version.hip,
+                     "torch": torch.__version__}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(m["batch"], spec, range(L),
+                                           kv_scales=FP8_SCALES if fp8 else None)
+    del m
+    torch.cuda.empty_cache()
+    # The second workload the decode is held to: the Llama-3-8B-shaped ragged batch, measured in
+    # the same run (8 layers of fresh data, so that no layer is read from the last-level cache).
+    if args.config == 4 and args.layers <= 0 and not args.no_secondary:
+        spec3 = dataclasses.replace(workloads.SPECS[3], num_layers=8,
+                                    block_size=args.block_size)
+        m3 = measure_decode(spec3, 40, 10, args.workgroups, fp8, args.fused, named_layers=True)
+        rec["secondary"] = {
+            "workload": m3["workload"],
+            "decode_launch_us": round(m3["decode_us"], 2),
+            "decode_launch_us_spread": m3["spread"],
+            "ms_per_step": round(m3["ms_step"], 4),
+            "value": round(m3["value"], 2), "unit": "GB/s",
+            "tokens_per_s_per_layer_step": round(spec3.num_seqs * 8 / (m3["ms_step"] * 1e-3), 1),
+            "decode_workgroups": m3["grid"],
+            "roofline": m3["roofline"]}
+        del m3
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline and "cpu_baseline" in rec:
+        rec["cpu_baseline"]["single_thread_by_workload"] = single_thread_rates()
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+FP8_SCALES = (0.05, 0.05)   # per-pool scales of the fp8 path (values do not change its cost)
+
+
+def measure_decode(spec, steps, warmup, nwg, fp8, fused, named_layers=False):
+    """Build a seeded batch of `spec` on the GPU and time it: back-to-back decode launches over
+    all layers (mean launch duration, and the spread of per-sweep means), then whole steps (per
+    layer: reshape_and_cache, then decode; or the fused launch). Returns the timings, the roofline
+    record and the batch."""
+    import torch
+    import paged_kv_cache_452_amd as pkv
+    import workloads
+
+    dev = "cuda"
     B = spec.block_size
     t = workloads.make_tables(spec)
-    fp8 = args.kv_dtype == "fp8"
-    ks, vs = 0.05, 0.05   # per-pool scales of the fp8 path (values do not change its cost)
+    ks, vs = FP8_SCALES
     if fp8:
         batch = workloads.make_batch_fp8(spec, device=dev, tables=t)
     else:
@@ -393,7 +539,6 @@ def main() -> int:
     S, Hq, Hkv, D, L = (spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                         spec.num_layers)
     max_ctx = int(t.context_lens.max())
-    nwg = args.workgroups
     ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, B, max_ctx, nwg),
                            dev)
     outs = torch.empty((L, S, Hq, D), dtype=batch.q.dtype, device=dev)
@@ -409,7 +554,12 @@ def main() -> int:
                                   t.num_blocks, B, stream)
 
     def decode(i, k, v):
-        if fp8:
+        if fused:
+            pkv.paged_attention_decode_append(outs[i], batch.q, batch.new_key, batch.new_value,
+                                              k, v, batch.block_tables, batch.context_lens,
+                                              spec.scale, Hq, Hkv, D, B, max_ctx, nwg, ws, stream,
+                                              kv_scales=(ks, vs) if fp8 else None)
+        elif fp8:
             pkv.paged_attention_decode_fp8(outs[i], batch.q, k, v, batch.block_tables,
                                            batch.context_lens, spec.scale, ks, vs, Hq, Hkv, D, B,
                                            max_ctx, nwg, ws, stream)
@@ -418,44 +568,23 @@ def main() -> int:
                                        batch.context_lens, spec.scale, Hq, Hkv, D, B, max_ctx,
                                        nwg, ws, stream)
 
-    def fused(i, k, v):
-        pkv.paged_attention_decode_append(outs[i], batch.q, batch.new_key, batch.new_value, k, v,
-                                          batch.block_tables, batch.context_lens, spec.scale, Hq,
-                                          Hkv, D, B, max_ctx, nwg, ws, stream,
-                                          kv_scales=(ks, vs) if fp8 else None)
-
     def step():
         for i, (k, v) in enumerate(layers):
-            if not args.fused:
+            if not fused:
                 cache(k, v)
-                decode(i, k, v)
-            else:
-                fused(i, k, v)
+            decode(i, k, v)
 
     def sweep_decode():
         for i, (k, v) in enumerate(layers):
-            if not args.fused:
-                decode(i, k, v)
-            else:
-                fused(i, k, v)
+            decode(i, k, v)
 
-    def timed(fn, reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b)
-
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     # Timed region B: the decode kernel alone, launched back to back over the layers; the mean
     # launch duration is the region's time over the launch count. An event after every sweep
     # (between launches, not inside any) also gives the spread of the per-sweep means.
-    reps_b = max(1, args.steps // 2)
+    reps_b = max(1, steps // 2)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps_b + 1)]
     torch.cuda.synchronize()
     marks[0].record(stream)
@@ -465,77 +594,55 @@ def main() -> int:
     torch.cuda.synchronize()
     avg_decode_ms = marks[0].elapsed_time(marks[-1]) / (reps_b * L)
     sweep_us = [marks[r].elapsed_time(marks[r + 1]) * 1e3 / L for r in range(reps_b)]
-    # Timed region A: whole steps (per layer: reshape_and_cache, then decode), no markers inside.
-    ms_total = timed(step, args.steps)
-    ms_step = ms_total / args.steps
+    # Timed region A: whole steps, no markers inside.
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / steps
 
-    per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=1 if fp8 else 2,
-                                   fused=args.fused)
-    value = per_launch * L / (ms_step * 1e-3) / 1e9
+    kv_elem = 1 if fp8 else 2
+    per_launch = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=kv_elem,
+                                   fused=fused)
     achieved = per_launch / (avg_decode_ms * 1e-3) / 1e9
-    workload = ((spec.name if args.layers <= 0 else f"{spec.name}, {L} layers") +
+    workload = ((spec.name if not named_layers else f"{spec.name}, {L} layers") +
                 ("" if B == 16 else f", block size {B}") + (", fp8 E4M3 KV" if fp8 else "") +
-                (", fused step" if args.fused else ""))
+                (", fused step" if fused else ""))
     traffic = measured_traffic(workload)
-    grid = nwg or pkv.paged_attention_num_workgroups(S, Hq, Hkv, max_ctx, B)
-    rec = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": spec.dtype,
-        "data": "synthetic",
-        "config": {"workload": workload, "num_seqs": S, "context_lens": "all 4096" if
-                   args.config == 4 else "seeded", "num_q_heads": Hq, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": B, "num_layers": L,
-                   "num_blocks_per_layer": t.num_blocks, "decode_workgroups": grid,
-                   "kv_dtype": "fp8 e4m3, one scale per pool" if fp8 else spec.dtype,
-                   "step": ("per layer: reshape_and_cache of the step's new tokens, then "
-                            "paged_attention_decode" if not args.fused else
-                            "per layer: one paged_attention_decode_append launch (the step's new "
-                            "tokens appended to the pool and attended to with the cached "
-                            "context)")},
-        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s_per_layer_step": round(S * L / (ms_step * 1e-3), 1),
-        "decode_launch_us": round(avg_decode_ms * 1e3, 2),
-        "decode_launch_us_spread": dict({k: round(v, 2) for k, v in percentiles(sweep_us).items()},
-                                        sweeps=reps_b, launches_per_sweep=L),
-        "timing": "roofline.achieved: back-to-back step launches of the decode kernel over all "
-                  "layers between two HIP events on the launch stream (mean launch duration), "
-                  "timed first; value: K whole steps between two HIP events",
+    res = {
+        "tables": t, "batch": batch, "workload": workload,
+        "grid": nwg or pkv.paged_attention_num_workgroups(S, Hq, Hkv, max_ctx, B),
+        "decode_us": avg_decode_ms * 1e3, "ms_step": ms_step,
+        "value": per_launch * L / (ms_step * 1e-3) / 1e9,
+        "spread": dict({k: round(v, 2) for k, v in percentiles(sweep_us).items()},
+                       sweeps=reps_b, launches_per_sweep=L),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "traffic_source": (f"{os.path.relpath(TRAFFIC_FILE, ROOT)}: L2-to-fabric "
+                                        "bytes per launch (rocprofv3 TCC_EA0 read requests of "
+                                        "32, 64 and 128 bytes and write requests of 32 and 64 "
+                                        "bytes, times their sizes) of this workload, taken on "
+                                        "the same decode code (hash of the kernel sources "
+                                        "without comments); gfx950 has no MALL counter, so MALL "
+                                        "hits are included") if traffic else None,
                      "algorithmic_bytes_per_launch": per_launch,
-                     "kernel": ("paged_attention_decode" if not args.fused else
+                     "kernel": ("paged_attention_decode" if not fused else
                                 "paged_attention_decode_append") +
                                " (one persistent decode kernel; split streams merged in it)"},
     }
-    uniq = unique_kv_bytes(t.block_tables, t.context_lens, Hkv, D, kv_elem=1 if fp8 else 2,
-                           block=B)
-    logical = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=1 if fp8 else 2) - \
+    uniq = unique_kv_bytes(t.block_tables, t.context_lens, Hkv, D, kv_elem=kv_elem, block=B)
+    logical = algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=kv_elem) - \
         algorithmic_bytes(t.context_lens, Hq, Hkv, D, block=B, kv_elem=0)
     if uniq < logical:   # blocks shared between sequences (a common prefix)
-        rec["unique_kv"] = {"bytes_per_launch": uniq, "logical_kv_bytes_per_launch": logical,
+        res["unique_kv"] = {"bytes_per_launch": uniq, "logical_kv_bytes_per_launch": logical,
                             "gbps_at_decode_time": round(uniq / (avg_decode_ms * 1e-3) / 1e9, 2),
                             "what": "K/V bytes counting each physical block once (a shared "
                                     "prefix is read by every sharer but stored once)"}
-    props = torch.cuda.get_device_properties(0)
-    rec["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
-                     "compute_units": props.multi_processor_count, "hip": torch.version.hip,
-                     "torch": torch.__version__}
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(batch, spec, range(L), kv_scales=(ks, vs) if fp8
-                                           else None)
-    print(json.dumps(rec), flush=True)
-    return 0
-
+    return res
 
 if __name__ == "__main__":
     sys.exit(main())
