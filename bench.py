@@ -488,17 +488,14 @@ def main() -> int:
     rec["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                      "compute_units": props.multi_processor_count, "hip": torch.version.hip,
                      "torch": torch.__version__}
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(m["batch"], spec, range(L),
-                                           kv_scales=FP8_SCALES if fp8 else None)
-    del m
-    torch.cuda.empty_cache()
     # The second workload the decode is held to: the Llama-3-8B-shaped ragged batch, measured in
-    # the same run (8 layers of fresh data, so that no layer is read from the last-level cache).
+    # the same run right after the first (8 layers of fresh data, so that no layer is read from
+    # the last-level cache; warmed up for at least 0.25 s so that the GPU clocks are settled).
     if args.config == 4 and args.layers <= 0 and not args.no_secondary:
         spec3 = dataclasses.replace(workloads.SPECS[3], num_layers=8,
                                     block_size=args.block_size)
-        m3 = measure_decode(spec3, 40, 10, args.workgroups, fp8, args.fused, named_layers=True)
+        m3 = measure_decode(spec3, 40, 10, args.workgroups, fp8, args.fused, named_layers=True,
+                            min_warmup_s=0.25)
         rec["secondary"] = {
             "workload": m3["workload"],
             "decode_launch_us": round(m3["decode_us"], 2),
@@ -510,7 +507,12 @@ def main() -> int:
             "roofline": m3["roofline"]}
         del m3
         torch.cuda.empty_cache()
-    if not args.no_cpu_baseline and "cpu_baseline" in rec:
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(m["batch"], spec, range(L),
+                                           kv_scales=FP8_SCALES if fp8 else None)
+    del m
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
         rec["cpu_baseline"]["single_thread_by_workload"] = single_thread_rates()
     print(json.dumps(rec), flush=True)
     return 0
@@ -519,11 +521,12 @@ def main() -> int:
 FP8_SCALES = (0.05, 0.05)   # per-pool scales of the fp8 path (values do not change its cost)
 
 
-def measure_decode(spec, steps, warmup, nwg, fp8, fused, named_layers=False):
+def measure_decode(spec, steps, warmup, nwg, fp8, fused, named_layers=False, min_warmup_s=0.0):
     """Build a seeded batch of `spec` on the GPU and time it: back-to-back decode launches over
     all layers (mean launch duration, and the spread of per-sweep means), then whole steps (per
-    layer: reshape_and_cache, then decode; or the fused launch). Returns the timings, the roofline
-    record and the batch."""
+    layer: reshape_and_cache, then decode; or the fused launch). The warm-up runs `warmup` steps,
+    and more until min_warmup_s seconds have passed. Returns the timings, the roofline record and
+    the batch."""
     import torch
     import paged_kv_cache_452_amd as pkv
     import workloads
@@ -578,8 +581,13 @@ def measure_decode(spec, steps, warmup, nwg, fp8, fused, named_layers=False):
         for i, (k, v) in enumerate(layers):
             decode(i, k, v)
 
-    for _ in range(warmup):
+    t_warm = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_warm < min_warmup_s:
         step()
+        done += 1
+        if done >= warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     # Timed region B: the decode kernel alone, launched back to back over the layers; the mean
     # launch duration is the region's time over the launch count. An event after every sweep

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import helpers
 import oracle
 import paged_kv_cache_452_amd as pkv
 import workloads
@@ -514,3 +515,49 @@ def test_all_sequences_empty(num_workgroups):
                out=out)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_70b_shaped_block_size_32_step_every_row(fp8):
+    """The benchmark's block-size-32 workload (bench.py --block-size 32, with or without
+    --kv-dtype fp8): the 70B-shaped batch with 8,192 blocks of 32 tokens per layer, two layers.
+    For each layer, the step's scatter (whole K and V planes equal the oracle's, word for word or
+    byte for byte) then decode (every (sequence, head) row against the oracle)."""
+    spec = dataclasses.replace(workloads.SPECS[4], num_layers=2, block_size=32)
+    t = workloads.make_tables(spec)
+    B = 32
+    say("70B-shaped batch, block size 32, fp8" if fp8 else "70B-shaped batch, block size 32")
+    b = (workloads.make_batch_fp8 if fp8 else workloads.make_batch)(spec, device=DEV, tables=t)
+    S, Hq, Hkv, D = spec.num_seqs, spec.num_q_heads, spec.num_kv_heads, spec.head_dim
+    ks, vs = 0.5, 0.5
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, B, 4096), DEV)
+    out = torch.empty_like(b.q)
+    host = LayerHost(b.kv_pool[0])
+    key, value = b.new_key.cpu(), b.new_value.cpu()
+    for L in range(spec.num_layers):
+        kw, vw = host.planes(b.kv_pool[L])
+        if fp8:
+            oracle.reshape_and_cache8(kw, vw, key, value, oracle.BF16, ks, vs, t.slot_mapping,
+                                      Hkv, D, B, t.num_blocks)
+            pkv.reshape_and_cache_fp8(b.new_key, b.new_value, b.k_pool[L], b.v_pool[L],
+                                      b.slot_mapping, t.num_blocks, ks, vs, B)
+            pkv.paged_attention_decode_fp8(out, b.q, b.k_pool[L], b.v_pool[L], b.block_tables,
+                                           b.context_lens, spec.scale, ks, vs, Hq, Hkv, D, B,
+                                           4096, 0, ws)
+        else:
+            oracle.reshape_and_cache(kw, vw, key, value, t.slot_mapping, Hkv, D, B, t.num_blocks)
+            pkv.reshape_and_cache(b.new_key, b.new_value, b.k_pool[L], b.v_pool[L],
+                                  b.slot_mapping, t.num_blocks, B)
+            pkv.paged_attention_decode(out, b.q, b.k_pool[L], b.v_pool[L], b.block_tables,
+                                       b.context_lens, spec.scale, Hq, Hkv, D, B, 4096, 0, ws)
+        torch.cuda.synchronize()
+        assert host.equals(b.kv_pool[L], kw, vw), f"layer {L}: pool differs after the scatter"
+        if fp8:
+            ref = helpers.oracle_decode8(b.q, kw, vw, t.block_tables, t.context_lens, spec.scale,
+                                         ks, vs, Hq, Hkv, t.num_blocks, block_size=B)
+        else:
+            ref = oracle_decode(b.q, None, None, t.block_tables, t.context_lens, spec.scale, Hq,
+                                Hkv, t.num_blocks, k_words=kw, v_words=vw, block_size=B)
+        assert_close(out, ref, f"block size 32, layer {L}")
+    del b, host, ws
+    torch.cuda.empty_cache()
