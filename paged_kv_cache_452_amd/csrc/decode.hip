@@ -12,8 +12,8 @@
 // workgroups (one per compute unit) take ranges, which halves the streams the cut splits. A
 // workgroup's share is thus fixed whatever the mix of context lengths: a 32k-token sequence is
 // spread over many workgroups and a batch of short ones is packed into few, with no per-sequence
-// partition size to tune and no tail of idle compute units. Each workgroup derives the plan itself from context_lens (a prefix sum in LDS), so the
-// host needs no device data.
+// partition size to tune and no tail of idle compute units. Each workgroup derives the plan
+// itself from context_lens (a prefix sum in LDS), so the host needs no device data.
 //
 // Inside a range the four wavefronts interleave block by block (wave i takes positions
 // r0 + i, r0 + i + 4, ...), so all four always work on the same stream. Per 16-token block a
@@ -263,33 +263,13 @@ paged_decode_kernel(DecodeLaunch a) {
   // read on one XCD).
   const int T = uniform(s_ps[S]);  // units of one (kv head, head tile) over all sequences
   const int W = Hh * T;
-  int nwg = min((int)gridDim.x, W);
-  if (nwg == 0) return;  // no positions at all (every sequence empty): uniform over the launch
-  // Weighted ranges only when they can help and cannot hurt:
-  //  * every range keeps at least one position (W >= 2 nwg with weights in [kEvenWeight / 2,
-  //    kEvenWeight]): the split-stream bookkeeping needs non-empty ranges;
-  //  * the equal split does not already fall on stream boundaries (all streams of one length L
-  //    with W / nwg a whole number of streams): then it splits no stream, and any weighting
-  //    would add a merge to every workgroup. Every workgroup sees the same plan, so all decide
-  //    alike.
-  auto aligned_for = [&](int n) {
-    bool al = same_len && W % n == 0;
-    if (al) {
-      const int L = s_ps[1] - s_ps[0];  // units of every sequence
-      al = L > 0 && (W / n) % L == 0;
-    }
-    return al;
-  };
-  bool aligned = aligned_for(nwg);
-  // At most as many streams as workgroups, not cut evenly: the full grid would split nearly every
-  // stream; one workgroup per compute unit (the first half of the grid) splits half as many.
-  if (a.may_halve && !aligned && nwg >= 2) {
-    nwg /= 2;
-    aligned = aligned_for(nwg);
-  }
-  if ((int)blockIdx.x >= nwg) return;  // uniform over the workgroup
+  const int L = same_len ? uniform(s_ps[1] - s_ps[0]) : 0;  // units of every sequence, if equal
+  // Every workgroup sees the same plan, so all decide alike.
+  const RangePlan rp = plan_ranges(W, L, gridDim.x, a.may_halve, a.odd_weight);
+  const int nwg = rp.nwg;
+  if ((int)blockIdx.x >= nwg) return;  // uniform over the workgroup (nwg = 0: no positions)
   const int wg = range_of_workgroup(blockIdx.x, nwg);  // this workgroup's range
-  const int odd_w = W >= 2 * nwg && !aligned ? a.odd_weight : kEvenWeight;
+  const int odd_w = rp.odd_w;
   const int r0 = range_start(wg, nwg, W, odd_w);
   const int r1 = range_start(wg + 1, nwg, W, odd_w);
 

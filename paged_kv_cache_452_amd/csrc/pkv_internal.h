@@ -106,6 +106,35 @@ __host__ __device__ inline int range_owner(int p, int nwg, int W, int odd_weight
   return (int)(r < nwg - 1 ? r : nwg - 1);
 }
 
+// How a launch of `grid` workgroups cuts W positions: the workgroups that get a range (the rest
+// exit) and the weight of odd-XCD ranges. L is the units of every sequence when all sequences have
+// the same number, else 0.
+//  * Weighted ranges only when they can help and cannot hurt: every range must keep at least one
+//    position (W >= 2 nwg, weights in [kEvenWeight / 2, kEvenWeight]), since the split-stream
+//    bookkeeping needs non-empty ranges; and the equal split must not already fall on stream
+//    boundaries (all streams of length L with W / nwg a whole number of streams), where it splits
+//    no stream and any weighting would add a merge to every workgroup.
+//  * may_halve (the host chose a full grid and there are at most as many streams as workgroups):
+//    when the equal split would cut streams, one workgroup per compute unit (the first half of
+//    the grid) cuts half as many.
+struct RangePlan {
+  int nwg;       // workgroups with a range: 0 .. nwg - 1
+  int odd_w;     // range weight on odd XCDs (kEvenWeight: equal ranges)
+  bool aligned;  // equal ranges of W / nwg positions, each a whole number of streams
+};
+
+__host__ __device__ inline RangePlan plan_ranges(int W, int L, int grid, bool may_halve,
+                                                 int odd_weight) {
+  int nwg = grid < W ? grid : W;
+  auto aligned_for = [&](int n) { return L > 0 && W % n == 0 && (W / n) % L == 0; };
+  bool aligned = nwg > 0 && aligned_for(nwg);
+  if (may_halve && !aligned && nwg >= 2) {
+    nwg /= 2;
+    aligned = aligned_for(nwg);
+  }
+  return RangePlan{nwg, W >= 2 * nwg && !aligned ? odd_weight : kEvenWeight, aligned};
+}
+
 struct DecodeLaunch {
   void* out;
   const void* q;
@@ -134,7 +163,7 @@ struct DecodeLaunch {
   float v_inv;
   int odd_weight;       // range weight of workgroups on odd XCDs (even ones: kEvenWeight)
   int may_halve;        // the library chose a full grid and there are at most as many streams
-                        // as workgroups: the kernel may use half of them (see the kernel)
+                        // as workgroups: the kernel may use half of them (plan_ranges)
 };
 
 // Launch the decode kernel on `grid` workgroups (append: the fused variant that takes each

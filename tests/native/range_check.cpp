@@ -63,6 +63,34 @@ int main() {
       }
     }
   }
+  // plan_ranges: never more workgroups than the grid or the positions, at least one when there
+  // are positions; the full count unless may_halve, else the full count or its half; an aligned
+  // plan cuts W into equal ranges of whole L-unit streams and weighs nothing; weights only where
+  // every range keeps a position.
+  const int Ls[] = {0, 1, 3, 16, 64, 256, 512};
+  const int grids[] = {1, 2, 7, 8, 64, 128, 256, 512, 1024};
+  for (int L : Ls) {
+    for (int streams : {1, 7, 64, 256, 512, 513, 1280, 4096}) {
+      const long long Wl = (long long)streams * (L > 0 ? L : 37);
+      if (Wl >= 2147483647LL) continue;
+      const int W = (int)Wl;
+      for (int grid : grids) {
+        for (int halve = 0; halve < 2; ++halve) {
+          const RangePlan p = plan_ranges(W, L, grid, halve != 0, 900);
+          const int full = grid < W ? grid : W;
+          ++checked;
+          bool ok = p.nwg >= 1 && p.nwg <= full;
+          ok = ok && (halve ? (p.nwg == full || p.nwg == full / 2) : p.nwg == full);
+          if (p.aligned)
+            ok = ok && L > 0 && W % p.nwg == 0 && (W / p.nwg) % L == 0 && p.odd_w == kEvenWeight;
+          if (p.odd_w != kEvenWeight) ok = ok && !p.aligned && W >= 2 * p.nwg;
+          if (!ok && bad++ < 10)
+            printf("plan W=%d L=%d grid=%d halve=%d -> nwg=%d odd_w=%d aligned=%d\n", W, L, grid,
+                   halve, p.nwg, p.odd_w, (int)p.aligned);
+        }
+      }
+    }
+  }
   printf("ranges checked %lld, failures %lld\n", checked, bad);
   return bad ? 1 : 0;
 }
