@@ -28,9 +28,10 @@
 //   * keeps an online softmax with a lazily moved reference maximum: the reference m only moves
 //     (and the running sum and output get rescaled) when a score exceeds it by more than 2^8,
 //     so probabilities stay <= 256 and the common path needs no cross-lane traffic;
-//   * accumulates O[head][dim] += P[head][token] . V_tile[token][dim] with v_mfma_f32_16x16x16,
-//     P split into a 16-bit high part and a 16-bit residual so the product keeps fp32-level
-//     precision of P.
+//   * accumulates O[head][dim] += P[head][token] . V_tile[token][dim] with v_mfma_f32_16x16x16:
+//     against bf16 V, P split into a bf16 high part and a bf16 residual, so the product keeps
+//     fp32-level precision of P; against fp16 V (fp16 pools, and fp8 pools widened to fp16), one
+//     fp16 P, whose 11-bit significand keeps its relative error within 2^-12.
 // Tiles are prefetched RING-1 blocks ahead through a ring of registers that runs across stream
 // boundaries, and nothing else is read from memory on the common path: block ids come from a
 // register window of 64 per wavefront, and the q rows of the range's first streams are copied
@@ -140,6 +141,13 @@ struct Elem<false> {
     hi = __builtin_bit_cast(u32x2, h);
     lo = __builtin_bit_cast(u32x2, l);
   }
+  // p rounded to fp16 (11-bit significand: relative error at most 2^-12), packed in lane order.
+  static __device__ __forceinline__ u32x2 round(const float p[4]) {
+    f16x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (_Float16)p[e];
+    return __builtin_bit_cast(u32x2, h);
+  }
   static __device__ __forceinline__ unsigned short store(float x) {
     return __builtin_bit_cast(unsigned short, (_Float16)x);
   }
@@ -175,6 +183,12 @@ template <int D, bool BF16, bool KV8, bool APPEND, int RING>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void
 paged_decode_kernel(DecodeLaunch a) {
   using E = Elem<BF16>;
+  // Element type of the PV product. Against fp16 V -- fp16 pools, and fp8 pools, whose codes
+  // widen exactly to fp16 whatever q's type -- P is one fp16 value (relative error at most
+  // 2^-12). Against bf16 V it is a bf16 high part plus a bf16 residual: a bf16 P alone would
+  // carry errors up to 2^-9.
+  constexpr bool kSingleP = KV8 || !BF16;
+  using EV = Elem<!kSingleP>;
   constexpr int NQ = D / 32;                 // QK matrix ops (32-dim chunks) per block
   constexpr int NK = KV8 ? D / 64 : D / 32;  // 16-byte K loads per block
   constexpr int NV = KV8 ? D / 64 : D / 32;  // 16-byte V loads per block
@@ -760,8 +774,13 @@ paged_decode_kernel(DecodeLaunch a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    u32x2 phi, plo;
-    E::split(pr, phi, plo);
+    // P operand(s): one fp16 P against fp16 V; a bf16 high part and residual against bf16 V.
+    u32x2 phi, plo = u32x2{0u, 0u};
+    if constexpr (kSingleP) {
+      phi = EV::round(pr);
+    } else {
+      E::split(pr, phi, plo);
+    }
 
     // Ragged last block: zero V of dead slots (they may hold anything, NaN included).
     if ((j + 1) * kBlock > cur.n) {
@@ -796,13 +815,13 @@ paged_decode_kernel(DecodeLaunch a) {
       if constexpr (KV8) {
         // fp8 V: load i/4, dword i%4 holds this lane's 4 tokens of dim 16i + hl.
         const u32x4 w = vc[i / 4];
-        vv = E::from_fp8((i & 3) == 0 ? w.x : (i & 3) == 1 ? w.y : (i & 3) == 2 ? w.z : w.w);
+        vv = EV::from_fp8((i & 3) == 0 ? w.x : (i & 3) == 1 ? w.y : (i & 3) == 2 ? w.z : w.w);
       } else {
         const u32x4 w = vc[i / 2];
         vv = (i & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
       }
-      o[i] = E::pv(phi, vv, o[i]);
-      o[i] = E::pv(plo, vv, o[i]);
+      o[i] = EV::pv(phi, vv, o[i]);
+      if constexpr (!kSingleP) o[i] = EV::pv(plo, vv, o[i]);
     }
   };
 
