@@ -33,21 +33,21 @@ def _need_gpu():
 # name: (S, Hq, Hkv, D, B, lens rule, max_context_len, workgroups)
 CASES = {
     # 512 streams of 64 units on the default 512 workgroups: one whole stream per range.
-    "hit, full blocks": (64, 64, 8, 128, 16, "full", 1024, 0),
+    "full blocks": (64, 64, 8, 128, 16, "full", 1024, 0),
     # Same units, fewer tokens: the last block of each sequence is partly dead.
-    "hit, partly filled last blocks": (64, 64, 8, 128, 16, "last block ragged", 1024, 0),
+    "partly filled last blocks": (64, 64, 8, 128, 16, "last block ragged", 1024, 0),
     # 256 streams of 128 units: the library picks all 512 workgroups, and its half grid gives
     # one whole stream per range.
-    "hit on the half grid": (32, 32, 8, 128, 16, "full", 2048, 0),
+    "half grid": (32, 32, 8, 128, 16, "full", 2048, 0),
     # 128 workgroups over 512 streams of 16 units: four whole streams per range.
-    "hit, four streams per range": (64, 8, 8, 64, 16, "full", 256, 128),
+    "four streams per range": (64, 8, 8, 64, 16, "full", 256, 128),
     # 8 streams of 512 units on 8 workgroups: 128 positions per wave, two windows of tile ids.
-    "hit, two windows per wave": (8, 8, 1, 128, 16, "full", 8192, 8),
+    "two windows per wave": (8, 8, 1, 128, 16, "full", 8192, 8),
     # 64 streams of 128 units (64 blocks of 32 tokens) on 64 workgroups.
-    "hit, block size 32": (16, 32, 4, 64, 32, "full", 2048, 64),
+    "block size 32": (16, 32, 4, 64, 32, "full", 2048, 64),
     # Every sequence a unit short of max_context_len.
-    "miss, max_context_len above every length": (64, 64, 8, 128, 16, "full", 1040, 0),
-    "miss, one sequence a unit shorter": (64, 64, 8, 128, 16, "one short", 1024, 0),
+    "max_context_len above every length": (64, 64, 8, 128, 16, "all a unit short", 1040, 0),
+    "one sequence a unit shorter": (64, 64, 8, 128, 16, "one short", 1024, 0),
 }
 
 
@@ -56,6 +56,8 @@ def _lens(rule, S, max_ctx, rng):
         lens = np.full(S, max_ctx, np.int32)
     elif rule == "last block ragged":
         lens = (max_ctx - rng.integers(0, 16, size=S)).astype(np.int32)
+    elif rule == "all a unit short":
+        lens = np.full(S, max_ctx - 16, np.int32)
     elif rule == "one short":
         lens = np.full(S, max_ctx, np.int32)
         lens[S // 3] = max_ctx - 16
@@ -68,8 +70,6 @@ def _case(name, fp8):
     S, Hq, Hkv, D, B, rule, max_ctx, nwg = CASES[name]
     rng = np.random.default_rng(sum(map(ord, name)))
     lens = _lens(rule, S, max_ctx, rng)
-    if name.startswith("miss, max_context_len"):
-        lens[:] = max_ctx - 16  # one unit below the guess for every sequence
     spec = workloads.Spec(0, f"uniform start, {name}: S={S} Hq={Hq} Hkv={Hkv} D={D} B={B} "
                              f"max_ctx={max_ctx} workgroups={nwg}", S, Hq, Hkv, D, "bf16", 1,
                           seed=7, block_size=B)
@@ -109,8 +109,8 @@ def test_uniform_start_matches_oracle(name):
     assert_close(out, ref, spec.name)
 
 
-@pytest.mark.parametrize("name", ["hit, full blocks", "hit, partly filled last blocks",
-                                  "miss, one sequence a unit shorter"])
+@pytest.mark.parametrize("name", ["full blocks", "partly filled last blocks",
+                                  "one sequence a unit shorter"])
 def test_uniform_start_fp8_matches_oracle(name):
     spec, t, b, k, v, tables, bt, max_ctx, nwg = _case(name, fp8=True)
     k_scale, v_scale = 0.5, 0.25
