@@ -79,7 +79,7 @@ constexpr int kMergeRound = 4;
 
 // Tile buffers per wavefront (blocks in flight = kRing - 1), sized to stay within 256 VGPRs so
 // two workgroups fit on each compute unit. The same for fp8 tiles, which hold half the bytes:
-// 5 or 6 slots spill at d128, and 8 slots fit but measured no faster.
+// 5, 6 and 8 slots fit at d128 but measured slower.
 template <int D>
 constexpr int kRing = D == 128 ? 4 : 8;
 
