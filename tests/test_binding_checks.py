@@ -110,3 +110,12 @@ def test_reshape_refuses_malformed_arguments(fp8):
 def test_copy_blocks_refuses_int64_ids():
     with pytest.raises(ValueError, match="src_blocks: element type"):
         pkv.copy_blocks(None, torch.zeros(4, dtype=torch.int64), torch.zeros(4, dtype=torch.int32))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """With no built library and building switched off, loading raises: no path falls back to
+    anything that is not the HIP library."""
+    monkeypatch.setattr(pkv, "_lib", None)
+    monkeypatch.setattr(pkv, "LIB_PATH", str(tmp_path / "libpagedkv.so"))
+    with pytest.raises(RuntimeError, match="is not built"):
+        pkv.load_library(build_if_missing=False)
