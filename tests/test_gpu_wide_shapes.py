@@ -15,7 +15,7 @@ from helpers import (assert_close, gpu_decode, gpu_decode8, oracle_decode, oracl
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-MAX_COST = 4e9  # tokens x query heads x head dim: keeps each oracle run to seconds
+MAX_COST = 4e9  # tokens x query heads x head dim of a case: keeps each oracle run to seconds
 
 
 @pytest.fixture(autouse=True)
@@ -47,16 +47,20 @@ def wide_shape(seed: int):
     return Hkv * G, Hkv, D, B, dtype, lens, nwg
 
 
-CASES = [(seed, fp8) for seed in range(32) for fp8 in ((False, True) if seed % 4 == 0 else
-                                                        (False,))]
+def _small_enough(seed: int) -> bool:
+    Hq, _, D, _, _, lens, _ = wide_shape(seed)
+    return int(lens.sum()) * Hq * D <= MAX_COST
+
+
+# The first 32 seeds whose batch the oracle finishes in seconds; fp8 pools on every fourth.
+_SEEDS = [seed for seed in range(40) if _small_enough(seed)][:32]
+CASES = [(seed, fp8) for seed in _SEEDS for fp8 in ((False, True) if seed % 4 == 0 else (False,))]
 
 
 @pytest.mark.parametrize("seed,fp8", CASES)
 def test_wide_shape_matches_oracle(seed, fp8):
     Hq, Hkv, D, B, dtype, lens, nwg = wide_shape(seed)
     S = len(lens)
-    if int(lens.sum()) * Hq * D > MAX_COST:
-        pytest.skip("too large for a quick oracle run")
     spec = workloads.Spec(0, f"wide {seed}: S={S} Hq={Hq} Hkv={Hkv} D={D} B={B} {dtype} "
                              f"workgroups={nwg} fp8={fp8}", S, Hq, Hkv, D,
                           "bf16" if dtype == torch.bfloat16 else "fp16", 1, seed=seed,
