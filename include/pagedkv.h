@@ -30,7 +30,9 @@
  *   - Stateless and thread-safe: concurrent calls are fine as long as their outputs do not alias.
  *
  * Element types: bf16 (PKV_BF16) or IEEE fp16 (PKV_FP16); q, key, value, the pools and out all use
- * the same type. Accumulation is fp32.
+ * the same type. Accumulation is fp32. The softmax weights enter the weighted sum of V as a bf16
+ * value plus a bf16 residual for bf16 pools (fp32-level precision), and as one fp16 value for fp16
+ * pools (relative error at most 2^-12).
  *
  * Supported shapes: head_dim in {64, 128}; block_size in {16, 32} ("PagedAttention and KV Cache
  * Management", section "PagedAttention: OS Virtual Memory Architecture for GPUs": B = 16 or 32);
@@ -399,8 +401,9 @@ pkv_status kv_block_manager_tables(const pkv_block_manager* bm, const int64_t* s
  * paged_attention_decode over fp8 pools: as paged_attention_decode, with the key and value of a
  * slot taken as e4m3_value(code) * k_scale and e4m3_value(code) * v_scale. q and out are dtype
  * (bf16 or fp16); the pools hold E4M3 codes (PKV_FP8_E4M3 layout above). Accumulation is fp32;
- * the codes are widened exactly to dtype for the matrix cores, k_scale is applied to the scores
- * and v_scale to the normalised output. Workspace and errors as paged_attention_decode;
+ * key codes are widened exactly to dtype for the scores and value codes exactly to fp16 for the
+ * weighted sum, whose softmax weights enter as one fp16 value (relative error at most 2^-12);
+ * k_scale is applied to the scores and v_scale to the normalised output. Workspace and errors as paged_attention_decode;
  * k_scale, v_scale must be finite and > 0.
  */
 pkv_status paged_attention_decode_fp8(void* out, const void* q, const void* k_pool,
