@@ -1,0 +1,97 @@
+"""GPU: forty decode steps of a small serving loop driven by the host block manager, against the
+oracle. Every step appends one token to each live sequence (boundary allocation from the free
+list), copies shared partial blocks for copy-on-write (copy_blocks), scatters the new keys and
+values (reshape_and_cache), and every fifth step decodes all live sequences. Along the way
+sequences are forked, released and started, and the 14-block pool runs full, so blocks freed by
+released sequences are handed out again with their stale contents. The pool must equal the host
+model word for word at every decode, and the decode must match the oracle to the usual bar."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_452_amd as pkv
+import workloads
+from helpers import assert_close, gpu_decode, oracle_decode, say, words
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    yield
+    torch.cuda.synchronize()
+
+
+def test_serving_loop_matches_oracle():
+    Hq, Hkv, D, B, NB, MAXB = 16, 4, 128, 16, 14, 8
+    dt = torch.bfloat16
+    g = torch.Generator(device=DEV).manual_seed(2024)
+    kv = workloads.new_pool(1, NB, Hkv, B, D, dt, DEV).fill_(float("nan"))
+    k, v = (x[0] for x in workloads.planes(kv))
+    pool = pkv.kv_pool_create(kv, kv.numel() * 2, 1, NB, Hkv, D, B, pkv.PKV_BF16)
+    kw, vw = words(k), words(v)  # the host model of the pool
+    bm = pkv.BlockManager(NB, B)
+
+    def write(slots):
+        """New keys and values at `slots`, on the GPU and in the host model."""
+        n = len(slots)
+        key = workloads.randn((n, Hkv, D), dt, g, DEV)
+        val = workloads.randn((n, Hkv, D), dt, g, DEV)
+        pkv.reshape_and_cache(key, val, k, v, torch.from_numpy(slots).to(DEV), NB)
+        oracle.reshape_and_cache(kw, vw, key.cpu(), val.cpu(), slots, Hkv, D, B, NB)
+
+    def prompt(seq, n):
+        bm.allocate(seq, n)
+        bt, _ = bm.tables([seq], MAXB)
+        write(np.array([bt[0, i // B] * B + i % B for i in range(n)], np.int64))
+
+    for seq, n in ((0, 20), (1, 33), (2, 7)):
+        prompt(seq, n)
+    live = [0, 1, 2]
+    events = {5: ("fork", 1, 3), 12: ("release", 0), 16: ("prompt", 5, 40), 20: ("fork", 3, 4),
+              30: ("release", 2)}
+    copies_seen = decodes = 0
+    for step in range(40):
+        ev = events.get(step)
+        if ev is not None:
+            if ev[0] == "fork":
+                bm.fork(ev[1], ev[2])
+                live.append(ev[2])
+            elif ev[0] == "release":
+                bm.release(ev[1])
+                live.remove(ev[1])
+            else:
+                prompt(ev[1], ev[2])
+                live.append(ev[1])
+        slots, copies = bm.append(live)
+        if len(copies):
+            copies_seen += len(copies)
+            src = np.ascontiguousarray(copies[:, 0])
+            dst = np.ascontiguousarray(copies[:, 1])
+            pkv.copy_blocks(pool, torch.from_numpy(src).to(DEV), torch.from_numpy(dst).to(DEV))
+            for s_blk, d_blk in copies:
+                kw[d_blk] = kw[s_blk]
+                vw[d_blk] = vw[s_blk]
+        write(slots)
+        if step % 5 == 4:
+            bt, cl = bm.tables(live, MAXB)
+            say("serving loop step", step, "live", live, "lens", cl.tolist(), "free", bm.num_free)
+            q = workloads.randn((len(live), Hq, D), dt, g, DEV)
+            out = gpu_decode(q, k, v, torch.from_numpy(bt).to(DEV), torch.from_numpy(cl).to(DEV),
+                             D ** -0.5, Hq, Hkv, int(cl.max()))
+            torch.cuda.synchronize()
+            assert np.array_equal(words(k), kw) and np.array_equal(words(v), vw), \
+                f"step {step}: pool differs from the host model"
+            ref = oracle_decode(q, k, v, bt, cl, D ** -0.5, Hq, Hkv, NB, k_words=kw, v_words=vw)
+            assert_close(out, ref, f"serving loop step {step}")
+            decodes += 1
+    assert copies_seen == 2 and decodes == 8
+    assert bm.num_free == 0  # the pool ran full
+    for seq in list(live):
+        bm.release(seq)
+    assert bm.num_free == NB
+    pool.destroy()
