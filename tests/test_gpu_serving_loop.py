@@ -4,7 +4,8 @@ list), copies shared partial blocks for copy-on-write (copy_blocks), scatters th
 values (reshape_and_cache), and every fifth step decodes all live sequences. Along the way
 sequences are forked, released and started, and the 14-block pool runs full, so blocks freed by
 released sequences are handed out again with their stale contents. The pool must equal the host
-model word for word at every decode, and the decode must match the oracle to the usual bar."""
+model word for word at every decode, and the decode must match the oracle to the usual bar.
+The loop runs over a 16-bit pool and over an fp8 (E4M3) pool."""
 import numpy as np
 import pytest
 import torch
@@ -12,10 +13,13 @@ import torch
 import oracle
 import paged_kv_cache_452_amd as pkv
 import workloads
-from helpers import assert_close, gpu_decode, oracle_decode, say, words
+from helpers import (assert_close, codes, gpu_decode, gpu_decode8, oracle_decode, oracle_decode8,
+                     say, words)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+E4M3_NAN = 0x7F
+K_SCALE, V_SCALE = 0.5, 0.25
 
 
 @pytest.fixture(autouse=True)
@@ -26,14 +30,20 @@ def _need_gpu():
     torch.cuda.synchronize()
 
 
-def test_serving_loop_matches_oracle():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_serving_loop_matches_oracle(fp8):
     Hq, Hkv, D, B, NB, MAXB = 16, 4, 128, 16, 14, 8
     dt = torch.bfloat16
     g = torch.Generator(device=DEV).manual_seed(2024)
-    kv = workloads.new_pool(1, NB, Hkv, B, D, dt, DEV).fill_(float("nan"))
+    if fp8:
+        kv = workloads.new_pool(1, NB, Hkv, B, D, torch.uint8, DEV).fill_(E4M3_NAN)
+        pool = pkv.kv_pool_create(kv, kv.numel(), 1, NB, Hkv, D, B, pkv.PKV_FP8_E4M3)
+    else:
+        kv = workloads.new_pool(1, NB, Hkv, B, D, dt, DEV).fill_(float("nan"))
+        pool = pkv.kv_pool_create(kv, kv.numel() * 2, 1, NB, Hkv, D, B, pkv.PKV_BF16)
     k, v = (x[0] for x in workloads.planes(kv))
-    pool = pkv.kv_pool_create(kv, kv.numel() * 2, 1, NB, Hkv, D, B, pkv.PKV_BF16)
-    kw, vw = words(k), words(v)  # the host model of the pool
+    raw = codes if fp8 else words
+    kw, vw = raw(k), raw(v)  # the host model of the pool
     bm = pkv.BlockManager(NB, B)
 
     def write(slots):
@@ -41,8 +51,14 @@ def test_serving_loop_matches_oracle():
         n = len(slots)
         key = workloads.randn((n, Hkv, D), dt, g, DEV)
         val = workloads.randn((n, Hkv, D), dt, g, DEV)
-        pkv.reshape_and_cache(key, val, k, v, torch.from_numpy(slots).to(DEV), NB)
-        oracle.reshape_and_cache(kw, vw, key.cpu(), val.cpu(), slots, Hkv, D, B, NB)
+        sm = torch.from_numpy(slots).to(DEV)
+        if fp8:
+            pkv.reshape_and_cache_fp8(key, val, k, v, sm, NB, K_SCALE, V_SCALE, B)
+            oracle.reshape_and_cache8(kw, vw, key.cpu(), val.cpu(), oracle.BF16, K_SCALE, V_SCALE,
+                                      slots, Hkv, D, B, NB)
+        else:
+            pkv.reshape_and_cache(key, val, k, v, sm, NB)
+            oracle.reshape_and_cache(kw, vw, key.cpu(), val.cpu(), slots, Hkv, D, B, NB)
 
     def prompt(seq, n):
         bm.allocate(seq, n)
@@ -81,13 +97,21 @@ def test_serving_loop_matches_oracle():
             bt, cl = bm.tables(live, MAXB)
             say("serving loop step", step, "live", live, "lens", cl.tolist(), "free", bm.num_free)
             q = workloads.randn((len(live), Hq, D), dt, g, DEV)
-            out = gpu_decode(q, k, v, torch.from_numpy(bt).to(DEV), torch.from_numpy(cl).to(DEV),
-                             D ** -0.5, Hq, Hkv, int(cl.max()))
+            bt_d, cl_d = torch.from_numpy(bt).to(DEV), torch.from_numpy(cl).to(DEV)
+            if fp8:
+                out = gpu_decode8(q, k, v, bt_d, cl_d, D ** -0.5, K_SCALE, V_SCALE, Hq, Hkv,
+                                  int(cl.max()))
+            else:
+                out = gpu_decode(q, k, v, bt_d, cl_d, D ** -0.5, Hq, Hkv, int(cl.max()))
             torch.cuda.synchronize()
-            assert np.array_equal(words(k), kw) and np.array_equal(words(v), vw), \
+            assert np.array_equal(raw(k), kw) and np.array_equal(raw(v), vw), \
                 f"step {step}: pool differs from the host model"
-            ref = oracle_decode(q, k, v, bt, cl, D ** -0.5, Hq, Hkv, NB, k_words=kw, v_words=vw)
-            assert_close(out, ref, f"serving loop step {step}")
+            if fp8:
+                ref = oracle_decode8(q, kw, vw, bt, cl, D ** -0.5, K_SCALE, V_SCALE, Hq, Hkv, NB)
+            else:
+                ref = oracle_decode(q, k, v, bt, cl, D ** -0.5, Hq, Hkv, NB, k_words=kw,
+                                    v_words=vw)
+            assert_close(out, ref, f"serving loop step {step} fp8={fp8}")
             decodes += 1
     assert copies_seen == 2 and decodes == 8
     assert bm.num_free == 0  # the pool ran full
