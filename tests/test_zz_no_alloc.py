@@ -79,3 +79,42 @@ def test_noalloc_two_calls_match_the_workspace_decode_and_the_oracle():
                        spec.num_q_heads, spec.num_kv_heads, b.max_context_len, nwg)
     torch.cuda.synchronize()
     assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_noalloc_decode_replays_in_a_graph():
+    """The no-alloc decode captured into a graph (torch.cuda.graph, on the capture stream) and
+    replayed four times, each with a new q copied in eagerly before it, and an eager call and
+    synchronizations between replays: every replay equals the eager call on the same q bit for
+    bit, and the first matches the oracle. The captured region holds the decode kernel only."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    rng = np.random.default_rng(909)
+    spec, t, b = _case(32, 8, 128, rng.integers(300, 3000, size=16), seed=91)
+    k, v = b.k_pool[0], b.v_pool[0]
+    args = (spec.scale, spec.num_q_heads, spec.num_kv_heads, spec.head_dim, 16,
+            b.max_context_len, 0)
+    _noalloc(spec, b, 0)  # the first call on a device finds and clears the scratch: not captured
+    torch.cuda.synchronize()
+    q_static = b.q.clone()
+    out_static = torch.full_like(b.q, 3.0)
+    graph = torch.cuda.CUDAGraph()
+    say("noalloc decode: capture")
+    with torch.cuda.graph(graph):
+        pkv.paged_attention_decode_noalloc(out_static, q_static, k, v, b.block_tables,
+                                           b.context_lens, *args)
+    gen = torch.Generator(device=DEV).manual_seed(92)
+    for r in range(4):
+        q_r = workloads.randn(tuple(b.q.shape), b.q.dtype, gen, DEV)
+        q_static.copy_(q_r)
+        say("noalloc decode: replay", r)
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = torch.full_like(b.q, 3.0)
+        pkv.paged_attention_decode_noalloc(eager, q_r, k, v, b.block_tables, b.context_lens, *args)
+        torch.cuda.synchronize()
+        assert torch.equal(out_static.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+        if r == 0:
+            ref = oracle_decode(q_r, k, v, t.block_tables, t.context_lens, spec.scale,
+                                spec.num_q_heads, spec.num_kv_heads, t.num_blocks)
+            assert_close(out_static, ref, "graph replay")
