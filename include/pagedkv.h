@@ -26,7 +26,8 @@
  *   - Device-resident indices (block table entries, context lengths, slots) are NOT validated:
  *     block ids must lie in [0, num_blocks), context lengths in [0, max_context_len] and
  *     [0, max_blocks_per_seq*block_size], and slots must be distinct within one call.
- *     Violations are undefined behaviour (out-of-bounds device accesses).
+ *     Violations are undefined behaviour (out-of-bounds device accesses). On request,
+ *     paged_attention_check_inputs counts them on the device (a debug aid).
  *   - Stateless and thread-safe: concurrent calls are fine as long as their outputs do not alias.
  *
  * Element types: bf16 (PKV_BF16) or IEEE fp16 (PKV_FP16); q, key, value, the pools and out all use
@@ -487,6 +488,36 @@ pkv_status paged_attention_decode_noalloc(void* out, const void* q, const void* 
                                           int block_size, int num_seqs, int max_blocks_per_seq,
                                           int max_context_len, int num_workgroups,
                                           pkv_dtype dtype, hipStream_t stream);
+
+/*
+ * Debug check of a step's index inputs, on the device, reading nothing but them (never the pool,
+ * so it is safe on the very inputs it is meant to catch). The decode and scatter kernels trust
+ * these indices: a sequence's table must name pool blocks that hold its tokens ("PagedAttention
+ * and KV Cache Management", section "PagedAttention: OS Virtual Memory Architecture for GPUs"),
+ * and every new token owns one slot ("How Block Paging Operates During Generation").
+ * Counts, written to result (device int32 [4], 4-byte aligned):
+ *   result[0]  used table entries outside [0, num_blocks): block_tables[s][j] for
+ *              j < ceil(n / block_size), n = context_lens[s] clamped to
+ *              [0, max_blocks_per_seq * block_size] as the decode clamps it;
+ *   result[1]  context lengths outside [0, min(max_context_len, max_blocks_per_seq * block_size)];
+ *   result[2]  slots equal to an earlier non-negative slot of slot_mapping (repeats);
+ *   result[3]  slots at or past num_blocks * block_size (reshape_and_cache skips them).
+ *   block_tables device int32 [num_seqs][max_blocks_per_seq]; context_lens device int32
+ *                [num_seqs]; slot_mapping device int64 [num_tokens], or NULL with
+ *                num_tokens == 0.
+ * The counts are written by kernels on `stream`: read them once it has finished. The repeat
+ * count compares each slot with every earlier one (quadratic in num_tokens): a debug aid, not for
+ * every step of a serving loop.
+ * Errors: PKV_ERR_INVALID_ARG (negative sizes, num_blocks or block_size < 1, NULL where data is
+ * read: context_lens when num_seqs > 0, block_tables when there are table entries, slot_mapping
+ * when num_tokens > 0), PKV_ERR_UNSUPPORTED (sizes past 32-bit indexing), PKV_ERR_ALIGNMENT,
+ * PKV_ERR_HIP.
+ */
+pkv_status paged_attention_check_inputs(const int32_t* block_tables, const int32_t* context_lens,
+                                        int num_seqs, int max_blocks_per_seq, int max_context_len,
+                                        int block_size, int num_blocks,
+                                        const int64_t* slot_mapping, int num_tokens,
+                                        int32_t* result, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* pkv_status_string(pkv_status status);

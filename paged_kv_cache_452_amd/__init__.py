@@ -30,6 +30,7 @@ EXPORTED = ("kv_pool_bytes", "kv_pool_create", "kv_pool_layer", "kv_pool_destroy
             "kv_block_manager_allocate", "kv_block_manager_fork", "kv_block_manager_append",
             "kv_block_manager_release", "kv_block_manager_tables", "kv_block_manager_num_free_host",
             "kv_block_manager_swap_out", "kv_block_manager_swap_in", "pkv_status_string",
+            "paged_attention_check_inputs",
             "paged_attention_decode_noalloc")
 
 PKV_NOALLOC_SCRATCH_BYTES = 17043456  # include/pagedkv.h
@@ -86,6 +87,8 @@ def load_library(build_if_missing: bool = True):
     lib.paged_attention_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i,
                                                    i, i, vp]
     lib.paged_attention_decode_noalloc.restype = i
+    lib.paged_attention_check_inputs.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp]
+    lib.paged_attention_check_inputs.restype = i
     lib.paged_attention_decode_append_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f, f, f, i,
                                                       i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.paged_attention_decode_append_fp8.restype = i
@@ -371,6 +374,33 @@ def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, context
         float(scale), num_q_heads, num_kv_heads, head_dim, block_size, S,
         block_tables.shape[1], max_context_len, num_workgroups, _dtype_code(q),
         _stream(stream)))
+
+
+def paged_attention_check_inputs(block_tables, context_lens, num_blocks: int,
+                                 block_size: int = 16, max_context_len: Optional[int] = None,
+                                 slot_mapping=None, stream=None) -> dict:
+    """Debug check of a step's index inputs on the device (never reads the pool). Waits for the
+    device and returns the counts: bad_table_entries (used entries outside [0, num_blocks)),
+    bad_context_lens, repeated_slots and slots_past_pool (slot_mapping, when given)."""
+    import torch
+    _int_tensor("block_tables", block_tables, torch.int32, 2)
+    S, max_blocks = block_tables.shape
+    _int_tensor("context_lens", context_lens, torch.int32, 1, S)
+    T = 0
+    if slot_mapping is not None:
+        _int_tensor("slot_mapping", slot_mapping, torch.int64, 1)
+        T = slot_mapping.shape[0]
+    _require_cuda(block_tables, context_lens, slot_mapping)
+    if max_context_len is None:
+        max_context_len = max_blocks * block_size
+    result = torch.empty(4, dtype=torch.int32, device=block_tables.device)
+    _check("paged_attention_check_inputs", load_library().paged_attention_check_inputs(
+        _ptr(block_tables), _ptr(context_lens), S, max_blocks, max_context_len, block_size,
+        num_blocks, _ptr(slot_mapping), T, _ptr(result), _stream(stream)))
+    torch.cuda.synchronize(result.device)
+    c = result.cpu().tolist()
+    return dict(bad_table_entries=c[0], bad_context_lens=c[1], repeated_slots=c[2],
+                slots_past_pool=c[3])
 
 
 def reshape_and_cache_fp8(key, value, k_pool, v_pool, slot_mapping, num_blocks: int,

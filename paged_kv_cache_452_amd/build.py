@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "decode.hip", "cache.hip", "block_manager.cpp"]
+SOURCES = ["api.hip", "decode.hip", "cache.hip", "check.hip", "block_manager.cpp"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

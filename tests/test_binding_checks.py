@@ -119,3 +119,32 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(pkv, "LIB_PATH", str(tmp_path / "libpagedkv.so"))
     with pytest.raises(RuntimeError, match="is not built"):
         pkv.load_library(build_if_missing=False)
+
+
+def test_check_inputs_refuses_malformed_arguments():
+    bt = torch.zeros(S, 4, dtype=torch.int32)
+    cl = torch.zeros(S, dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensors required"):
+        pkv.paged_attention_check_inputs(bt, cl, 10)
+    for kw, what in ((dict(block_tables=bt.long()), "block_tables: element type"),
+                     (dict(context_lens=torch.zeros(S + 1, dtype=torch.int32)), "context_lens: 4"),
+                     (dict(slot_mapping=torch.zeros(5, dtype=torch.int32)),
+                      "slot_mapping: element type")):
+        args = dict(block_tables=bt, context_lens=cl)
+        args.update(kw)
+        with pytest.raises(ValueError, match=what):
+            pkv.paged_attention_check_inputs(args["block_tables"], args["context_lens"], 10,
+                                             slot_mapping=kw.get("slot_mapping"))
+
+
+def test_check_inputs_status_codes_without_a_launch():
+    """Invalid sizes are refused before any device work (addresses are never dereferenced)."""
+    lib = pkv.load_library()
+    f = lib.paged_attention_check_inputs
+    fake = 1 << 40
+    assert f(fake, fake, -1, 4, 64, 16, 10, None, 0, fake, None) == -1      # negative num_seqs
+    assert f(fake, fake, 2, 4, 64, 16, 0, None, 0, fake, None) == -1        # no blocks
+    assert f(fake, fake, 2, 4, 64, 16, 10, None, 3, fake, None) == -1       # slots missing
+    assert f(fake, fake, 2, 4, 64, 16, 10, None, 0, None, None) == -1       # no result buffer
+    assert f(fake, fake + 1, 2, 4, 64, 16, 10, None, 0, fake, None) == -3   # misaligned lengths
+    assert f(fake, fake, 2, 1 << 28, 64, 16, 10, None, 0, fake, None) == -2 # past 32-bit indexing
