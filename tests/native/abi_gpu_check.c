@@ -1,6 +1,7 @@
 /* The decode path driven from plain C, with no Python or PyTorch: device memory from hipMalloc,
  * a one-layer bf16 pool described by kv_pool_create, every token's key and value scattered by
- * reshape_and_cache, then paged_attention_decode with the library's choice of grid. Four
+ * reshape_and_cache, then paged_attention_decode with the library's choice of grid, and
+ * paged_attention_check_inputs of the same inputs (all counts zero). Four
  * sequences of 1, 15, 16 and 41 tokens; the 41-token one uses the page's block table [7, 3, 9]
  * ("KV-Cache Management and PagedAttention", section "PagedAttention: treat the cache like
  * virtual memory"). Inputs come from a fixed linear congruential generator. The program writes
@@ -95,7 +96,21 @@ int main(int argc, char** argv) {
   PKV_CHECK(paged_attention_decode(d_out, d_q, k_layer, v_layer, (const int32_t*)d_tables,
                                    (const int32_t*)d_lens, 1.0f / sqrtf((float)D), HQ, HKV, D, B,
                                    S, MAXB, MAXCTX, 0, PKV_BF16, d_ws, ws_bytes, 0));
+  /* The debug check of the same inputs: clean, so every count is zero. */
+  void* d_counts;
+  int32_t counts[4] = {-1, -1, -1, -1};
+  HIP_CHECK(hipMalloc(&d_counts, sizeof counts));
+  PKV_CHECK(paged_attention_check_inputs((const int32_t*)d_tables, (const int32_t*)d_lens, S, MAXB,
+                                         MAXCTX, B, NB, (const int64_t*)d_slots, T,
+                                         (int32_t*)d_counts, 0));
   HIP_CHECK(hipDeviceSynchronize());
+  HIP_CHECK(hipMemcpy(counts, d_counts, sizeof counts, hipMemcpyDeviceToHost));
+  HIP_CHECK(hipFree(d_counts));
+  if (counts[0] || counts[1] || counts[2] || counts[3]) {
+    fprintf(stderr, "input check counted %d %d %d %d\n", counts[0], counts[1], counts[2],
+            counts[3]);
+    return 4;
+  }
   HIP_CHECK(hipMemcpy(out, d_out, sizeof out, hipMemcpyDeviceToHost));
   unsigned char* pool_host = malloc(pool_bytes);
   if (!pool_host) return 1;
