@@ -201,9 +201,14 @@ def _rows(name: str, t, shape, dtype=None):
         raise ValueError(f"{name}: must be contiguous")
 
 
-def _plane(name: str, t, dtype):
+def _plane(name: str, t, dtype, tile: int = 0, tiles: Optional[int] = None):
     """A pool plane: a view whose last dimension is dense (the K or V tiles of one layer), of the
-    pool's element type."""
+    pool's element type. The K and V tiles of a (block, kv head) alternate in the pool, so the
+    kernels address the n tiles of a plane across 2n - 1 tiles of memory from its first element:
+    with `tile` (elements per tile) given, the tensor's storage must hold that span from the view
+    on. n is `tiles` when the caller knows it (num_blocks * num_kv_heads), else the tiles the view
+    itself covers. A compact copy of a plane (half that span) is refused here, before any launch
+    could write or read past its end."""
     import torch
     if isinstance(t, int):
         return
@@ -213,6 +218,15 @@ def _plane(name: str, t, dtype):
         raise ValueError(f"{name}: element type {t.dtype}, expected {dtype}")
     if t.dim() == 0 or (t.shape[-1] > 1 and t.stride(-1) != 1):
         raise ValueError(f"{name}: the last dimension must be dense")
+    if tile > 0:
+        n = tiles if tiles is not None else t.numel() // tile
+        span = (2 * n - 1) * tile if n > 0 else 0
+        held = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+        if held < span:
+            raise ValueError(
+                f"{name}: its storage holds {held} elements from this view, but the {n} tiles of "
+                f"a plane span {span} (K and V tiles alternate): pass a plane of the pool "
+                "(a view), not a copy")
 
 
 def _workspace(t):
@@ -224,7 +238,7 @@ def _workspace(t):
 
 
 def _decode_args(name, out, q, k_pool, v_pool, block_tables, context_lens, num_q_heads,
-                 head_dim, pool_dtype=None):
+                 head_dim, block_size, pool_dtype=None):
     """Checks shared by the decode bindings. Returns the number of sequences."""
     import torch
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
@@ -233,8 +247,8 @@ def _decode_args(name, out, q, k_pool, v_pool, block_tables, context_lens, num_q
     _rows("q", q, (S, num_q_heads, head_dim))
     _rows("out", out, (S, num_q_heads, head_dim), q.dtype)
     pd = q.dtype if pool_dtype is None else pool_dtype
-    _plane("k_pool", k_pool, pd)
-    _plane("v_pool", v_pool, pd)
+    _plane("k_pool", k_pool, pd, block_size * head_dim)
+    _plane("v_pool", v_pool, pd, block_size * head_dim)
     _int_tensor("block_tables", block_tables, torch.int32, 2, S)
     _int_tensor("context_lens", context_lens, torch.int32, 1, S)
     return S
@@ -306,8 +320,8 @@ def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, num_blocks: int,
     T, Hkv, D = key.shape
     _rows("key", key, (T, Hkv, D))
     _rows("value", value, (T, Hkv, D), key.dtype)
-    _plane("k_pool", k_pool, key.dtype)
-    _plane("v_pool", v_pool, key.dtype)
+    _plane("k_pool", k_pool, key.dtype, block_size * D, num_blocks * Hkv)
+    _plane("v_pool", v_pool, key.dtype, block_size * D, num_blocks * Hkv)
     _int_tensor("slot_mapping", slot_mapping, torch.int64, 1, T, address_ok=True)
     _require_cuda(key, value, k_pool, v_pool, slot_mapping)
     _check("reshape_and_cache", load_library().reshape_and_cache(
@@ -347,7 +361,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, s
                            stream=None) -> None:
     """out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s over each sequence's paged K/V."""
     S = _decode_args("paged_attention_decode", out, q, k_pool, v_pool, block_tables,
-                     context_lens, num_q_heads, head_dim)
+                     context_lens, num_q_heads, head_dim, block_size)
     _workspace(workspace)
     _require_cuda(out, q, k_pool, v_pool, block_tables, context_lens, workspace)
     max_blocks = block_tables.shape[1]
@@ -367,7 +381,7 @@ def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, context
     split-stream state, so the call allocates nothing. Calls that overlap in time on one device
     race (they share that scratch); calls ordered on one stream are safe."""
     S = _decode_args("paged_attention_decode_noalloc", out, q, k_pool, v_pool, block_tables,
-                     context_lens, num_q_heads, head_dim)
+                     context_lens, num_q_heads, head_dim, block_size)
     _require_cuda(out, q, k_pool, v_pool, block_tables, context_lens)
     _check("paged_attention_decode_noalloc", load_library().paged_attention_decode_noalloc(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
@@ -414,8 +428,8 @@ def reshape_and_cache_fp8(key, value, k_pool, v_pool, slot_mapping, num_blocks: 
     T, Hkv, D = key.shape
     _rows("key", key, (T, Hkv, D))
     _rows("value", value, (T, Hkv, D), key.dtype)
-    _plane("k_pool", k_pool, torch.uint8)
-    _plane("v_pool", v_pool, torch.uint8)
+    _plane("k_pool", k_pool, torch.uint8, block_size * D, num_blocks * Hkv)
+    _plane("v_pool", v_pool, torch.uint8, block_size * D, num_blocks * Hkv)
     _int_tensor("slot_mapping", slot_mapping, torch.int64, 1, T, address_ok=True)
     _require_cuda(key, value, k_pool, v_pool, slot_mapping)
     _check("reshape_and_cache_fp8", load_library().reshape_and_cache_fp8(
@@ -432,7 +446,7 @@ def paged_attention_decode_fp8(out, q, k_pool, v_pool, block_tables, context_len
     """paged_attention_decode over fp8 (E4M3) pools with per-pool scales."""
     import torch
     S = _decode_args("paged_attention_decode_fp8", out, q, k_pool, v_pool, block_tables,
-                     context_lens, num_q_heads, head_dim, pool_dtype=torch.uint8)
+                     context_lens, num_q_heads, head_dim, block_size, pool_dtype=torch.uint8)
     _workspace(workspace)
     _require_cuda(out, q, k_pool, v_pool, block_tables, context_lens, workspace)
     max_blocks = block_tables.shape[1]
@@ -474,7 +488,7 @@ def paged_attention_decode_append(out, q, key, value, k_pool, v_pool, block_tabl
     kv_scales=(k_scale, v_scale) for fp8 pools."""
     import torch
     S = _decode_args("paged_attention_decode_append", out, q, k_pool, v_pool, block_tables,
-                     context_lens, num_q_heads, head_dim,
+                     context_lens, num_q_heads, head_dim, block_size,
                      pool_dtype=None if kv_scales is None else torch.uint8)
     _rows("key", key, (S, num_kv_heads, head_dim), q.dtype)
     _rows("value", value, (S, num_kv_heads, head_dim), q.dtype)

@@ -107,6 +107,57 @@ def test_reshape_refuses_malformed_arguments(fp8):
             call(**kw)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_compact_copies_of_planes_are_refused(fp8):
+    """The K and V tiles of a (block, kv head) alternate in the pool, so the kernels address a
+    plane of n tiles across 2n - 1 tiles of memory. A compact copy of a plane holds only n: every
+    binding that takes planes refuses it before any launch, while the planes of a real pool (the
+    last layer's V plane ends exactly at the pool's end) pass on to the device check."""
+    pool_t = torch.uint8 if fp8 else torch.bfloat16
+    pool = torch.zeros(3, 10, HKV, 2, B * D, dtype=pool_t)   # [layer][block][kv head][K, V]
+    k, v = pool[2].select(-2, 0), pool[2].select(-2, 1)
+    a = _decode_args(k_pool=k, v_pool=v)
+    key = torch.zeros(S, HKV, D, dtype=torch.bfloat16)
+    sm = torch.zeros(S, dtype=torch.int64)
+
+    def calls(k, v):
+        if fp8:
+            yield lambda: pkv.reshape_and_cache_fp8(key, key, k, v, sm, 10, 1.0, 1.0)
+            yield lambda: pkv.paged_attention_decode_fp8(
+                a["out"], a["q"], k, v, a["block_tables"], a["context_lens"], 0.125, 1.0, 1.0, HQ,
+                HKV, D, B, 64)
+            yield lambda: pkv.paged_attention_decode_append(
+                a["out"], a["q"], key, key, k, v, a["block_tables"], a["context_lens"], 0.125, HQ,
+                HKV, D, B, 64, kv_scales=(1.0, 1.0))
+        else:
+            yield lambda: pkv.reshape_and_cache(key, key, k, v, sm, 10)
+            yield lambda: pkv.paged_attention_decode(
+                a["out"], a["q"], k, v, a["block_tables"], a["context_lens"], 0.125, HQ, HKV, D,
+                B, 64)
+            yield lambda: pkv.paged_attention_decode_noalloc(
+                a["out"], a["q"], k, v, a["block_tables"], a["context_lens"], 0.125, HQ, HKV, D,
+                B, 64)
+            yield lambda: pkv.paged_attention_decode_append(
+                a["out"], a["q"], key, key, k, v, a["block_tables"], a["context_lens"], 0.125, HQ,
+                HKV, D, B, 64)
+
+    for call in calls(k, v):
+        with pytest.raises(ValueError, match="device tensors required"):
+            call()
+    for name, kk, vv in (("k_pool", k.clone(), v), ("v_pool", k, v.clone())):
+        for call in calls(kk, vv):
+            with pytest.raises(ValueError, match=f"{name}: .* not a copy"):
+                call()
+    # reshape_and_cache: a pool of fewer blocks than num_blocks says is refused too
+    small = torch.zeros(6, HKV, 2, B * D, dtype=pool_t)
+    with pytest.raises(ValueError, match="k_pool: .* not a copy"):
+        if fp8:
+            pkv.reshape_and_cache_fp8(key, key, small.select(-2, 0), small.select(-2, 1), sm, 10,
+                                      1.0, 1.0)
+        else:
+            pkv.reshape_and_cache(key, key, small.select(-2, 0), small.select(-2, 1), sm, 10)
+
+
 def test_copy_blocks_refuses_int64_ids():
     with pytest.raises(ValueError, match="src_blocks: element type"):
         pkv.copy_blocks(None, torch.zeros(4, dtype=torch.int64), torch.zeros(4, dtype=torch.int32))
