@@ -37,7 +37,8 @@ def test_model_reproduces_the_printed_allocator_run():
 
 
 def test_on_demand_and_boundary_allocation_examples():
-    # "a 25-token prompt with B = 16 allocates exactly 2 physical blocks"
+    # on-demand allocation: with 16-token blocks, a 25-token prompt takes two physical blocks
+    # ("PagedAttention and KV Cache Management", "How Block Paging Operates During Generation")
     m = BlockManagerModel(8, 16)
     assert len(m.allocate(0, 25)) == 2
     # tokens 26..32 stay in block 1; the 33rd token crosses the boundary and pops block 2
