@@ -16,6 +16,7 @@
 namespace {
 
 constexpr int kCheckCounts = 4;  // bad table entries, bad lengths, repeated slots, slots past pool
+constexpr int kCheckThreads = 256;  // threads of a check workgroup (the launch and the LDS tile)
 
 struct CheckLaunch {
   const int32_t* block_tables;  // [num_seqs][max_blocks]
@@ -42,7 +43,7 @@ __device__ __forceinline__ unsigned wave_sum(unsigned v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void check_inputs_kernel(CheckLaunch a) {
+__global__ __launch_bounds__(kCheckThreads) void check_inputs_kernel(CheckLaunch a) {
   const long nthreads = (long)gridDim.x * blockDim.x;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   unsigned bad_entries = 0u, bad_lens = 0u, repeats = 0u, past = 0u;
@@ -68,18 +69,48 @@ __global__ __launch_bounds__(256) void check_inputs_kernel(CheckLaunch a) {
       if (n < 0 || n > a.max_tokens) ++bad_lens;
     }
   }
-  // Slots: past the pool, and repeats (a non-negative slot equal to an earlier one).
-  for (long i = gid; i < a.num_tokens; i += nthreads) {
-    const int64_t si = a.slot_mapping[i];
-    if (si >= a.num_slots) ++past;
-    if (si >= 0) {
-      for (long k = 0; k < i; ++k) {
-        if (a.slot_mapping[k] == si) {
-          ++repeats;
-          break;
+  // Slots: past the pool, and repeats (a non-negative slot equal to an earlier one). A workgroup
+  // takes 256 consecutive tokens at a time (thread tid: token base + tid) and walks the slots
+  // before them in tiles of 256 staged in LDS, each thread comparing its slot with the tile's
+  // entries that precede it, 16 at a time (their LDS reads in flight together). The next tile's
+  // entry is loaded into a register before the compares, so its latency hides behind them. The
+  // loops are uniform over the workgroup (they depend on the base and num_tokens only), so every
+  // thread reaches every barrier.
+  constexpr int kCmp = 16;
+  __shared__ int64_t s_tile[kCheckThreads];
+  for (long base = (long)blockIdx.x * kCheckThreads; base < a.num_tokens;
+       base += (long)gridDim.x * kCheckThreads) {
+    const long i = base + threadIdx.x;
+    const bool live = i < a.num_tokens;
+    const int64_t si = live ? a.slot_mapping[i] : -1;
+    if (live && si >= a.num_slots) ++past;
+    bool found = false;
+    const long kend = base + kCheckThreads < a.num_tokens ? base + kCheckThreads : a.num_tokens;
+    int64_t next = (long)threadIdx.x < a.num_tokens ? a.slot_mapping[threadIdx.x] : -1;
+    for (long k0 = 0; k0 < kend; k0 += kCheckThreads) {
+      __syncthreads();  // the previous tile is no longer read
+      s_tile[threadIdx.x] = next;
+      __syncthreads();
+      const long kn = k0 + kCheckThreads + threadIdx.x;
+      next = (k0 + kCheckThreads < kend && kn < a.num_tokens) ? a.slot_mapping[kn] : -1;
+      if (live && si >= 0 && !found) {
+        const long before = i - k0;  // entries of this tile that precede token i
+        const int n = before < kCheckThreads ? (int)before : kCheckThreads;
+        for (int k1 = 0; k1 < n; k1 += kCmp) {
+          int64_t e[kCmp];
+#pragma unroll
+          for (int u = 0; u < kCmp; ++u) e[u] = s_tile[k1 + u];
+          bool hit = false;
+#pragma unroll
+          for (int u = 0; u < kCmp; ++u) hit |= (k1 + u < n) & (e[u] == si);
+          if (hit) {
+            found = true;
+            break;
+          }
         }
       }
     }
+    if (found) ++repeats;
   }
   bad_entries = wave_sum(bad_entries);
   bad_lens = wave_sum(bad_lens);
@@ -127,9 +158,10 @@ extern "C" pkv_status paged_attention_check_inputs(
   hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, stream, a.result);
   const long entries = (long)num_seqs * (max_blocks_per_seq > 0 ? max_blocks_per_seq : 1);
   const long work = entries > num_tokens ? entries : (long)num_tokens;
-  long blocks = (work + 255) / 256;
+  long blocks = (work + kCheckThreads - 1) / kCheckThreads;
   if (blocks < 1) blocks = 1;
   if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(check_inputs_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(check_inputs_kernel, dim3((unsigned)blocks), dim3(kCheckThreads), 0, stream,
+                     a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -109,6 +109,28 @@ def test_random_corruption_counts_match_the_host(seed):
     assert got == want
 
 
+def test_prefill_sized_slot_mapping():
+    """20,000 slots of one long sequence (the search runs over LDS tiles of 256 earlier slots):
+    repeats planted across tile edges, far apart and at the very end, plus skipped and
+    past-the-pool slots, counted exactly as the host counts them."""
+    T, B = 20000, 16
+    NB = T // B + 4
+    lens = np.array([T], np.int32)
+    tables = np.arange(NB - 4, dtype=np.int32)[None]
+    slots = np.arange(T, dtype=np.int64)
+    for dst, src in ((256, 255), (512, 0), (4096, 4095), (19999, 7), (12345, 12344),
+                     (767, 511)):
+        slots[dst] = slots[src]
+    slots[100] = -1
+    slots[300] = NB * B + 3
+    slots[301] = NB * B + 3  # past the pool and a repeat
+    want = host_counts(tables, lens, T, B, NB, slots)
+    assert want["repeated_slots"] == 7 and want["slots_past_pool"] == 2
+    got = gpu_counts(tables, lens, NB, B, T, slots)
+    say("check inputs, prefill-sized", got)
+    assert got == want
+
+
 def test_empty_inputs():
     got = gpu_counts(np.zeros((0, 4), np.int32), np.zeros(0, np.int32), 10, 16, 64, None)
     assert got == dict.fromkeys(KEYS, 0)
