@@ -561,3 +561,43 @@ def test_70b_shaped_block_size_32_step_every_row(fp8):
         assert_close(out, ref, f"block size 32, layer {L}")
     del b, host, ws
     torch.cuda.empty_cache()
+
+
+def test_planes_given_as_device_addresses():
+    """The bindings take a layer's planes as tensors or as the device addresses kv_pool_layer
+    gives. Both forms reach the same kernels: reshape_and_cache then decode on the last layer of
+    a three-layer pool, once each way from the same starting pool, leave the same pool and give
+    the same outputs bit for bit, and those match the oracle."""
+    L, S, Hq, Hkv, D, B = 3, 6, 16, 4, 128, 16
+    lens = np.array([1, 15, 16, 17, 300, 1000], np.int32)
+    spec = workloads.Spec(0, "planes as addresses", S, Hq, Hkv, D, "bf16", L, seed=61)
+    t = workloads.make_tables(spec, lens=lens, seed=61)
+    b = workloads.make_batch(spec, device=DEV, tables=t)
+    for layer in range(L):
+        poison_dead_slots_(b.k_pool[layer], b.v_pool[layer], t.block_tables, lens, Hkv, D)
+    pool = pkv.kv_pool_create(b.kv_pool, b.kv_pool.numel() * 2, L, t.num_blocks, Hkv, D, B,
+                              pkv.PKV_BF16)
+    try:
+        ka, va = pkv.kv_pool_layer(pool, L - 1)
+    finally:
+        pkv.kv_pool_destroy(pool)
+    k, v = b.k_pool[L - 1], b.v_pool[L - 1]
+    assert (ka, va) == (k.data_ptr(), v.data_ptr())
+    start = b.kv_pool.clone()
+    results = []
+    for kk, vv in ((k, v), (ka, va)):
+        b.kv_pool.copy_(start)
+        say("planes as", "addresses" if isinstance(kk, int) else "views")
+        pkv.reshape_and_cache(b.new_key, b.new_value, kk, vv, b.slot_mapping, t.num_blocks, B)
+        out = torch.full_like(b.q, 3.0)
+        ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, B,
+                                                                   int(lens.max()), 0), DEV)
+        pkv.paged_attention_decode(out, b.q, kk, vv, b.block_tables, b.context_lens, spec.scale,
+                                   Hq, Hkv, D, B, int(lens.max()), 0, ws)
+        torch.cuda.synchronize()
+        results.append((out, b.kv_pool.clone()))
+    (o1, p1), (o2, p2) = results
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(p1.view(torch.int16), p2.view(torch.int16))
+    ref = oracle_decode(b.q, k, v, t.block_tables, lens, spec.scale, Hq, Hkv, t.num_blocks)
+    assert_close(o2, ref, "planes as device addresses")
