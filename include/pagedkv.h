@@ -28,6 +28,8 @@
  *     [0, max_blocks_per_seq*block_size], and slots must be distinct within one call.
  *     Violations are undefined behaviour (out-of-bounds device accesses). On request,
  *     paged_attention_check_inputs counts them on the device (a debug aid).
+ *   - A call's output (out; the pool for the scatter calls) must not overlap its other inputs:
+ *     the kernels read inputs while they write the output.
  *   - Stateless and thread-safe: concurrent calls are fine as long as their outputs do not alias.
  *
  * Element types: bf16 (PKV_BF16) or IEEE fp16 (PKV_FP16); q, key, value, the pools and out all use

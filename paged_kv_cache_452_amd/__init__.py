@@ -201,6 +201,23 @@ def _rows(name: str, t, shape, dtype=None):
         raise ValueError(f"{name}: must be contiguous")
 
 
+def _disjoint(name: str, t, others) -> None:
+    """The output tensor `t` shares no byte with any of `others` ((name, tensor) pairs; device
+    addresses and None are skipped). The kernels read their inputs while they write the output,
+    so an output that overlaps an input is refused rather than left to the order of the writes."""
+    if not hasattr(t, "data_ptr"):
+        return
+    a0 = t.data_ptr()
+    a1 = a0 + t.numel() * t.element_size()
+    for other_name, o in others:
+        if not hasattr(o, "data_ptr") or o.numel() == 0 or t.numel() == 0:
+            continue
+        b0 = o.data_ptr()
+        b1 = b0 + o.numel() * o.element_size()
+        if a0 < b1 and b0 < a1:
+            raise ValueError(f"{name}: must not overlap {other_name}")
+
+
 def _plane(name: str, t, dtype, tile: int = 0, tiles: Optional[int] = None):
     """A pool plane: a view whose last dimension is dense (the K or V tiles of one layer), of the
     pool's element type. The K and V tiles of a (block, kv head) alternate in the pool, so the
@@ -246,6 +263,7 @@ def _decode_args(name, out, q, k_pool, v_pool, block_tables, context_lens, num_q
     S = q.shape[0]
     _rows("q", q, (S, num_q_heads, head_dim))
     _rows("out", out, (S, num_q_heads, head_dim), q.dtype)
+    _disjoint("out", out, (("q", q),))
     pd = q.dtype if pool_dtype is None else pool_dtype
     _plane("k_pool", k_pool, pd, block_size * head_dim)
     _plane("v_pool", v_pool, pd, block_size * head_dim)
@@ -492,6 +510,7 @@ def paged_attention_decode_append(out, q, key, value, k_pool, v_pool, block_tabl
                      pool_dtype=None if kv_scales is None else torch.uint8)
     _rows("key", key, (S, num_kv_heads, head_dim), q.dtype)
     _rows("value", value, (S, num_kv_heads, head_dim), q.dtype)
+    _disjoint("out", out, (("key", key), ("value", value)))
     _workspace(workspace)
     _require_cuda(out, q, key, value, k_pool, v_pool, block_tables, context_lens, workspace)
     max_blocks = block_tables.shape[1]

@@ -158,6 +158,27 @@ def test_compact_copies_of_planes_are_refused(fp8):
             pkv.reshape_and_cache(key, key, small.select(-2, 0), small.select(-2, 1), sm, 10)
 
 
+def test_outputs_overlapping_inputs_are_refused():
+    """out must not share memory with q (nor, for the fused step, with the new key and value
+    rows): the kernels read those while they write out. Exact aliasing and partial overlap are
+    both refused before any launch; disjoint halves of one buffer pass on to the device check."""
+    a = _decode_args()
+    with pytest.raises(ValueError, match="out: must not overlap q"):
+        _decode(q=a["q"], out=a["q"])
+    buf = torch.zeros(2 * S + 1, HQ, D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out: must not overlap q"):
+        _decode(q=buf[:S], out=buf[1:S + 1])
+    with pytest.raises(ValueError, match="device tensors required"):
+        _decode(q=buf[:S], out=buf[S:2 * S])
+    rows = torch.zeros(S, HQ, D, dtype=torch.bfloat16)
+    key = rows.view(-1)[:S * HKV * D].view(S, HKV, D)
+    good = torch.zeros(S, HKV, D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out: must not overlap key"):
+        pkv.paged_attention_decode_append(rows, a["q"], key, good, a["k_pool"], a["v_pool"],
+                                          a["block_tables"], a["context_lens"], 0.125, HQ, HKV,
+                                          D, B, 64)
+
+
 def test_copy_blocks_refuses_int64_ids():
     with pytest.raises(ValueError, match="src_blocks: element type"):
         pkv.copy_blocks(None, torch.zeros(4, dtype=torch.int64), torch.zeros(4, dtype=torch.int32))
