@@ -322,7 +322,7 @@ def bench_swap(args) -> int:
     spec = workloads.SPECS[4]
     t = workloads.make_tables(spec)
     L, NB, Hkv, D, B = spec.num_layers, t.num_blocks, spec.num_kv_heads, spec.head_dim, 16
-    kv = workloads.new_pool(L, NB, Hkv, B, D, torch.bfloat16, "cuda")
+    kv = workloads.new_pool(L, NB, Hkv, B, D, torch.bfloat16, "cuda").zero_()
     victims = np.concatenate([t.block_tables[0], t.block_tables[1]]).astype(np.int32)
     n = victims.shape[0]
     hkv = workloads.new_pool(L, n, Hkv, B, D, torch.bfloat16, "cpu", pin_memory=True)
@@ -359,6 +359,54 @@ def bench_swap(args) -> int:
     flat_d.copy_(flat_h, non_blocking=True)
     ms_d2h = timed(lambda: flat_h.copy_(flat_d, non_blocking=True), reps)
     ms_h2d = timed(lambda: flat_d.copy_(flat_h, non_blocking=True), reps)
+    # The copy-engine path (swap_blocks_dma): ids on the host, one strided copy per block.
+    dev_h = np.ascontiguousarray(victims)
+    host_h = np.arange(n, dtype=np.int32)
+    dma_out = lambda st: pkv.swap_blocks_dma(dpool, hpool, dev_h, host_h, pkv.PKV_SWAP_OUT, st)
+    dma_in = lambda st: pkv.swap_blocks_dma(dpool, hpool, host_h, dev_h, pkv.PKV_SWAP_IN, st)
+    dma_out(stream)
+    dma_in(stream)
+    ms_dma_out = timed(lambda: dma_out(stream), reps)
+    ms_dma_in = timed(lambda: dma_in(stream), reps)
+    # A decode sweep over all layers of the 64-sequence batch on one stream, alone and while each
+    # kind of swap out runs on another (the swap outlasts the sweep).
+    Hq = spec.num_q_heads
+    S = spec.num_seqs
+    gq = torch.Generator(device="cuda").manual_seed(11)
+    q = workloads.randn((S, Hq, D), torch.bfloat16, gq, "cuda")
+    k_planes, v_planes = workloads.planes(kv)
+    bt = torch.from_numpy(t.block_tables).cuda()
+    cl = torch.from_numpy(t.context_lens).cuda()
+    max_ctx = int(t.context_lens.max())
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(S, Hq, Hkv, D, B, max_ctx, 0),
+                           "cuda")
+    dec_out = torch.empty_like(q)
+    s_dec, s_swap = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+
+    def sweep(st):
+        for layer in range(L):
+            pkv.paged_attention_decode(dec_out, q, k_planes[layer], v_planes[layer], bt, cl,
+                                       spec.scale, Hq, Hkv, D, B, max_ctx, 0, ws, st)
+
+    def decode_ms(swap_fn):
+        times = []
+        for _ in range(3):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            if swap_fn is not None:
+                swap_fn(s_swap)
+            a.record(s_dec)
+            sweep(s_dec)
+            e.record(s_dec)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(e))
+        return sorted(times)[1]
+
+    sweep(s_dec)
+    kernel_out = lambda st: pkv.swap_blocks(dpool, hpool, dev_ids, host_ids, pkv.PKV_SWAP_OUT, st)
+    beside = {"decode_alone_ms": decode_ms(None),
+              "beside_swap_blocks_ms": decode_ms(kernel_out),
+              "beside_swap_blocks_dma_ms": decode_ms(dma_out)}
     gbs = lambda ms: moved / (ms * 1e-3) / 1e9
     out_gbs, in_gbs = gbs(ms_out), gbs(ms_in)
     rt = 2 * moved / ((ms_out + ms_in) * 1e-3) / 1e9
@@ -381,6 +429,14 @@ def bench_swap(args) -> int:
                                "pool and back", "bytes_per_call": moved},
         "swap_out_ms": round(ms_out, 3), "swap_out_gbs": round(out_gbs, 2),
         "swap_in_ms": round(ms_in, 3), "swap_in_gbs": round(in_gbs, 2),
+        "swap_blocks_dma": {"out_ms": round(ms_dma_out, 3), "out_gbs": round(gbs(ms_dma_out), 2),
+                            "in_ms": round(ms_dma_in, 3), "in_gbs": round(gbs(ms_dma_in), 2),
+                            "what": "the same swaps on the copy engines (one strided copy per "
+                                    "block, ids read on the host)"},
+        "decode_beside_swap_out": dict({k: round(v, 3) for k, v in beside.items()},
+                                       what=f"decode of all {L} layers of the 64-sequence batch "
+                                            "on one stream, alone and while a swap out runs on "
+                                            "another"),
         "dma_copy_same_bytes": {"d2h_gbs": round(gbs(ms_d2h), 2), "h2d_gbs": round(gbs(ms_h2d), 2),
                                 "what": "one contiguous pinned hipMemcpyAsync each way"},
         "roofline": {"bound": "host link", "achieved": round(rt, 2), "peak": PCIE_PEAK_GBS,

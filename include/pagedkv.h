@@ -314,6 +314,28 @@ pkv_status swap_blocks(const pkv_pool* device_pool, const pkv_pool* host_pool,
                        pkv_swap_dir direction, hipStream_t stream);
 
 /*
+ * swap_blocks on the GPU's copy engines instead of its compute units, for swaps that run while
+ * other work (a decode step of the sequences still running) uses the GPU on another stream. The
+ * same copies, directions and pool requirements as swap_blocks. Measured on MI355X, 2 sequences'
+ * blocks of the 70B-shaped pool (16 layers, 512 MiB each way): about 37 GB/s, where swap_blocks
+ * reaches about 56 GB/s. But a decode running beside it slows by 2-5%, where beside swap_blocks
+ * it takes 80% longer.
+ *   src_blocks, dst_blocks  int32 [num_pairs] in host memory (pinned or pageable), read during
+ *                the call: the caller may reuse them once it returns.
+ * Every id is checked before anything is enqueued: an id outside its pool refuses the whole call
+ * with PKV_ERR_INVALID_ARG. The copies (one strided copy per block, its region in every layer)
+ * are ordered on `stream`. Destinations must be distinct and must not be sources. The call costs
+ * about 2 us of host time per block. num_pairs in [0, 65535]; 0 is a no-op.
+ * Errors: PKV_ERR_INVALID_ARG (as swap_blocks, ids out of range, id arrays in device memory),
+ * PKV_ERR_HIP if the runtime
+ * refuses a copy (copies of earlier blocks may then already be enqueued).
+ */
+pkv_status swap_blocks_dma(const pkv_pool* device_pool, const pkv_pool* host_pool,
+                           const int32_t* src_blocks, const int32_t* dst_blocks, int num_pairs,
+                           pkv_swap_dir direction, hipStream_t stream);
+
+/*
+ * Host block manager: the bookkeeping of which physical blocks hold which sequence's tokens/*
  * Host block manager: the bookkeeping of which physical blocks hold which sequence's tokens
  * ("PagedAttention and KV Cache Management" (blog.sejan.dev), sections "How Block Paging Operates
  * During Generation" (on-demand and boundary allocation), "Advanced Memory Sharing: Prefix Caching

@@ -24,7 +24,7 @@ PKV_SWAP_IN = 1
 EXPORTED = ("kv_pool_bytes", "kv_pool_create", "kv_pool_layer", "kv_pool_destroy",
             "reshape_and_cache", "paged_attention_num_workgroups",
             "paged_attention_workspace_bytes", "paged_attention_decode", "copy_blocks",
-            "reshape_and_cache_fp8", "paged_attention_decode_fp8", "swap_blocks",
+            "reshape_and_cache_fp8", "paged_attention_decode_fp8", "swap_blocks", "swap_blocks_dma",
             "paged_attention_decode_append", "paged_attention_decode_append_fp8",
             "kv_block_manager_create", "kv_block_manager_destroy", "kv_block_manager_num_free",
             "kv_block_manager_allocate", "kv_block_manager_fork", "kv_block_manager_append",
@@ -95,6 +95,8 @@ def load_library(build_if_missing: bool = True):
     lib.copy_blocks.argtypes = [vp, vp, vp, i, vp]
     lib.swap_blocks.argtypes = [vp, vp, vp, vp, i, i, vp]
     lib.swap_blocks.restype = i
+    lib.swap_blocks_dma.argtypes = [vp, vp, vp, vp, i, i, vp]
+    lib.swap_blocks_dma.restype = i
     lib.copy_blocks.restype = i
     i64 = ctypes.c_int64
     lib.kv_block_manager_create.argtypes = [ctypes.POINTER(vp), i, i, i]
@@ -494,6 +496,36 @@ def swap_blocks(device_pool: "KVPool", host_pool: "KVPool", src_blocks, dst_bloc
     _check("swap_blocks", load_library().swap_blocks(device_pool._h, host_pool._h,
                                                      _ptr(src_blocks), _ptr(dst_blocks), n,
                                                      int(direction), _stream(stream)))
+
+
+def swap_blocks_dma(device_pool: "KVPool", host_pool: "KVPool", src_blocks, dst_blocks,
+                    direction: int, stream=None) -> None:
+    """swap_blocks on the GPU's copy engines: the same copies, for swaps that run beside a decode
+    on another stream, which they barely slow. src_blocks, dst_blocks: int32 ids in host memory
+    (1-D numpy arrays or CPU tensors), read during the call; an id outside its pool refuses the
+    whole call."""
+    import numpy as np
+    import torch
+    ptrs = []
+    for name, t in (("src_blocks", src_blocks), ("dst_blocks", dst_blocks)):
+        if isinstance(t, torch.Tensor):
+            if t.is_cuda:
+                raise ValueError(f"{name}: must be in host memory (the host reads it)")
+            if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+                raise ValueError(f"{name}: must be a contiguous 1-D int32 tensor")
+            ptrs.append((t.data_ptr(), t.numel()))
+        elif isinstance(t, np.ndarray):
+            if t.dtype != np.int32 or t.ndim != 1 or not t.flags.c_contiguous:
+                raise ValueError(f"{name}: must be a contiguous 1-D int32 array")
+            ptrs.append((t.ctypes.data, t.size))
+        else:
+            raise ValueError(f"{name}: expected an int32 numpy array or CPU tensor")
+    n = ptrs[0][1]
+    if ptrs[1][1] != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    _check("swap_blocks_dma", load_library().swap_blocks_dma(
+        device_pool._h, host_pool._h, ptrs[0][0] if n else None, ptrs[1][0] if n else None, n,
+        int(direction), _stream(stream)))
 
 
 def paged_attention_decode_append(out, q, key, value, k_pool, v_pool, block_tables, context_lens,

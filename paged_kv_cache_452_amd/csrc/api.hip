@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "pkv_internal.h"
+#include "pkv_link.h"
 
 struct pkv_pool {
   char* base;             // layer 0, block 0, kv head 0: its K tile, then its V tile
@@ -83,6 +84,17 @@ bool device_visible(const int32_t* p, const int32_t** dev) {
   }
   *dev = (const int32_t*)d;
   return true;
+}
+
+// True when the host may read p directly: host memory, pinned or pageable (the runtime does not
+// know pageable memory, which is fine), or managed memory. False for device memory.
+bool host_readable(const void* p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeArray;
 }
 
 // Range weight of decode workgroups on odd-numbered XCDs (even ones weigh pkv::kEvenWeight): the
@@ -330,8 +342,53 @@ pkv_status swap_blocks(const pkv_pool* device_pool, const pkv_pool* host_pool,
   c.dst_ids = dst_dev;
   c.src_blocks = out ? d.num_blocks : h.num_blocks;
   c.dst_blocks = out ? h.num_blocks : d.num_blocks;
-  const hipError_t err = pkv::launch_block_copy(c, d.num_layers, num_pairs, stream);
+  const hipError_t err = pkv::launch_block_copy_link(c, d.num_layers, num_pairs, stream);
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status swap_blocks_dma(const pkv_pool* device_pool, const pkv_pool* host_pool,
+                           const int32_t* src_blocks, const int32_t* dst_blocks, int num_pairs,
+                           pkv_swap_dir direction, hipStream_t stream) {
+  if (device_pool == nullptr || host_pool == nullptr || num_pairs < 0 || num_pairs > 65535)
+    return PKV_ERR_INVALID_ARG;
+  if (direction != PKV_SWAP_OUT && direction != PKV_SWAP_IN) return PKV_ERR_INVALID_ARG;
+  const pkv_pool& d = *device_pool;
+  const pkv_pool& h = *host_pool;
+  if (d.num_layers != h.num_layers || d.num_kv_heads != h.num_kv_heads ||
+      d.head_dim != h.head_dim || d.block_size != h.block_size || d.dtype != h.dtype)
+    return PKV_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PKV_OK;
+  if (src_blocks == nullptr || dst_blocks == nullptr) return PKV_ERR_INVALID_ARG;
+  if (!host_readable(src_blocks) || !host_readable(dst_blocks)) return PKV_ERR_INVALID_ARG;
+  // The copy engines take the pinned host pool by its host address; pageable memory is refused.
+  void* hdev = nullptr;
+  if (!pinned_device_address(h.base, h.layer_bytes * (size_t)h.num_layers, &hdev))
+    return PKV_ERR_INVALID_ARG;
+  const bool out = direction == PKV_SWAP_OUT;
+  const int src_n = out ? d.num_blocks : h.num_blocks;
+  const int dst_n = out ? h.num_blocks : d.num_blocks;
+  // Every id is checked before anything is enqueued: a refused call moves nothing.
+  for (int i = 0; i < num_pairs; ++i) {
+    if (src_blocks[i] < 0 || src_blocks[i] >= src_n || dst_blocks[i] < 0 ||
+        dst_blocks[i] >= dst_n)
+      return PKV_ERR_INVALID_ARG;
+  }
+  const size_t block_bytes = block_bytes_of(&d);
+  const char* src_base = out ? d.base : h.base;
+  char* dst_base = out ? h.base : d.base;
+  const size_t src_pitch = out ? d.layer_bytes : h.layer_bytes;
+  const size_t dst_pitch = out ? h.layer_bytes : d.layer_bytes;
+  const hipMemcpyKind kind = out ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+  // One strided copy per block: its region in every layer (block_bytes wide, num_layers rows, one
+  // layer stride apart on each side).
+  for (int i = 0; i < num_pairs; ++i) {
+    const char* src = src_base + (size_t)src_blocks[i] * block_bytes;
+    char* dst = dst_base + (size_t)dst_blocks[i] * block_bytes;
+    if (hipMemcpy2DAsync(dst, dst_pitch, src, src_pitch, block_bytes, (size_t)d.num_layers, kind,
+                         stream) != hipSuccess)
+      return PKV_ERR_HIP;
+  }
+  return PKV_OK;
 }
 
 int paged_attention_num_workgroups(int num_seqs, int num_q_heads, int num_kv_heads,

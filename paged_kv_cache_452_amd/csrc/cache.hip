@@ -8,6 +8,7 @@
 // tokens of one dim together, so V is eight 2-byte stores.
 
 #include "pkv_internal.h"
+#include "pkv_link.h"
 
 namespace pkv {
 namespace {
@@ -133,7 +134,64 @@ __global__ __launch_bounds__(256) void block_copy_kernel(BlockCopy c) {
   __builtin_nontemporal_store(w, (u32x4*)dst);
 }
 
+// The same copies over the host link (swapping), from a small fixed grid. The link moves about
+// 55 GB/s, far less than the compute units can issue, so kLinkWorkgroups workgroups with
+// kLinkUnroll 16-byte loads in flight per thread keep it busy (measured: swap in 57.4 GB/s and
+// swap out 54.9 GB/s, against 54.7 and 53.8 GB/s with one workgroup per 4 KiB as above). Fewer
+// workgroups do not spare a decode running beside the swap: compute-unit accesses to host memory
+// slow such a decode by ~80% whatever the grid, which the copy-engine path (swap_blocks_dma)
+// avoids. Each workgroup takes whole regions in turn: region r is pair r % num_pairs of layer
+// r / num_pairs. The block ids of its next region, which may sit in pinned host memory (a round
+// trip over the link), are read while the current region is copied.
+__global__ __launch_bounds__(256) void block_copy_link_kernel(BlockCopy c, int num_layers,
+                                                              int num_pairs) {
+  const long regions = (long)num_layers * num_pairs;
+  const int chunks = (int)(c.block_bytes / 16);
+  long r = blockIdx.x;
+  if (r >= regions) return;
+  int s = c.src_ids[r % num_pairs];
+  int d = c.dst_ids[r % num_pairs];
+  for (; r < regions; r += gridDim.x) {
+    const long rn = r + gridDim.x;
+    int sn = 0, dn = 0;
+    if (rn < regions) {
+      sn = c.src_ids[rn % num_pairs];
+      dn = c.dst_ids[rn % num_pairs];
+    }
+    if (s >= 0 && s < c.src_blocks && d >= 0 && d < c.dst_blocks) {
+      const size_t layer = (size_t)(r / num_pairs);
+      const char* src = c.src + layer * c.src_layer_bytes + (size_t)s * c.block_bytes;
+      char* dst = c.dst + layer * c.dst_layer_bytes + (size_t)d * c.block_bytes;
+      for (int k0 = threadIdx.x; k0 < chunks; k0 += 256 * kLinkUnroll) {
+        u32x4 w[kLinkUnroll];
+#pragma unroll
+        for (int u = 0; u < kLinkUnroll; ++u) {
+          const int k = k0 + 256 * u;
+          if (k < chunks) w[u] = __builtin_nontemporal_load((const u32x4*)(src + (size_t)k * 16));
+        }
+#pragma unroll
+        for (int u = 0; u < kLinkUnroll; ++u) {
+          const int k = k0 + 256 * u;
+          if (k < chunks) __builtin_nontemporal_store(w[u], (u32x4*)(dst + (size_t)k * 16));
+        }
+      }
+    }
+    s = sn;
+    d = dn;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_block_copy_link(const BlockCopy& c, int num_layers, int num_pairs,
+                                  hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const long regions = (long)num_layers * num_pairs;
+  const unsigned grid = (unsigned)(regions < kLinkWorkgroups ? regions : kLinkWorkgroups);
+  hipLaunchKernelGGL(block_copy_link_kernel, dim3(grid), dim3(256), 0, stream, c, num_layers,
+                     num_pairs);
+  return hipGetLastError();
+}
 
 hipError_t launch_block_copy(const BlockCopy& c, int num_layers, int num_pairs,
                              hipStream_t stream) {

@@ -149,6 +149,135 @@ def test_swap_refuses_pageable_host_pool_and_mismatched_geometry():
         p.destroy()
 
 
+@pytest.mark.parametrize("kind,D,B", [("bf16", 128, 16), ("fp16", 64, 16), ("fp8", 128, 16),
+                                      ("bf16", 128, 32)])
+def test_swap_dma_out_then_in_bit_exact(kind, D, B):
+    """swap_blocks_dma (copy engines, ids read on the host): the same round trip as the kernel
+    path, against the oracle's block copies, with ids given as numpy arrays and as pinned
+    tensors."""
+    L, NB, NBH, Hkv = 3, 40, 24, 4
+    (dkv, hkv), dpool, hpool = _pools(L, NB, NBH, Hkv, D, B, kind, seed=D + B + 1)
+    rng = np.random.default_rng(D * B + 1)
+    n = 10
+    dev_blocks = rng.permutation(NB)[:n].astype(np.int32)
+    host_blocks = rng.permutation(NBH)[:n].astype(np.int32)
+    dkb = _raw(dkv).reshape(L, NB, -1)
+    want_h = _raw(hkv).reshape(L, NBH, -1).copy()
+    _copy_host(want_h, dkb, zip(dev_blocks.tolist(), host_blocks.tolist()))
+    say("dma swap out", kind, D, B)
+    pkv.swap_blocks_dma(dpool, hpool, dev_blocks, host_blocks, pkv.PKV_SWAP_OUT)
+    torch.cuda.synchronize()
+    assert np.array_equal(_raw(hkv).reshape(L, NBH, -1), want_h)
+    assert np.array_equal(_raw(dkv).reshape(L, NB, -1), dkb)
+    g = torch.Generator(device=DEV).manual_seed(8)
+    idx = torch.from_numpy(dev_blocks.astype(np.int64)).to(DEV)
+    dkv[:, idx] = _fill(tuple(dkv[:, idx].shape), kind, g, DEV)
+    back = rng.permutation(NB)[:n].astype(np.int32)
+    dkb2 = _raw(dkv).reshape(L, NB, -1).copy()
+    _copy_host(dkb2, want_h, zip(host_blocks.tolist(), back.tolist()))
+    say("dma swap in", kind, D, B)
+    pkv.swap_blocks_dma(dpool, hpool, _ids(host_blocks, "host"), _ids(back, "host"),
+                        pkv.PKV_SWAP_IN)
+    torch.cuda.synchronize()
+    assert np.array_equal(_raw(dkv).reshape(L, NB, -1), dkb2)
+    for a, b in zip(dev_blocks, back):
+        assert np.array_equal(_raw(dkv[:, int(b)]).reshape(L, -1), dkb[:, a])
+    dpool.destroy()
+    hpool.destroy()
+
+
+def test_swap_dma_refusals_move_nothing():
+    """An id outside its pool refuses the whole call before anything is enqueued (the host pool
+    keeps every byte); id arrays in device memory are refused by the binding and, called
+    directly, by the library; a pageable host pool and mismatched geometry are refused too."""
+    L, NB, NBH, Hkv, D, B = 2, 16, 12, 2, 128, 16
+    (dkv, hkv), dpool, hpool = _pools(L, NB, NBH, Hkv, D, B, "bf16", seed=5)
+    before = _raw(hkv).copy()
+    ok_src, ok_dst = np.array([3, 7], np.int32), np.array([0, 11], np.int32)
+    for src, dst in (([3, NB], [0, 1]), ([3, -1], [0, 1]), ([3, 7], [0, NBH])):
+        with pytest.raises(pkv.PagedKVError) as e:
+            pkv.swap_blocks_dma(dpool, hpool, np.array(src, np.int32), np.array(dst, np.int32),
+                                pkv.PKV_SWAP_OUT)
+        assert e.value.status == -1
+    torch.cuda.synchronize()
+    assert np.array_equal(_raw(hkv), before)
+    with pytest.raises(ValueError, match="host memory"):
+        pkv.swap_blocks_dma(dpool, hpool, _ids(ok_src, "device"), ok_dst, pkv.PKV_SWAP_OUT)
+    dev_src, dev_dst = _ids(ok_src, "device"), _ids(ok_dst, "device")
+    rc = pkv.load_library().swap_blocks_dma(dpool._h, hpool._h, dev_src.data_ptr(),
+                                            dev_dst.data_ptr(), 2, pkv.PKV_SWAP_OUT, None)
+    assert rc == -1
+    with pytest.raises(ValueError, match="int32"):
+        pkv.swap_blocks_dma(dpool, hpool, ok_src.astype(np.int64), ok_dst, pkv.PKV_SWAP_OUT)
+    pg = _aligned_pageable((L, NBH, Hkv, 2, B * D))
+    ppool = pkv.kv_pool_create(pg, pg.numel() * 2, L, NBH, Hkv, D, B, pkv.PKV_BF16)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.swap_blocks_dma(dpool, ppool, ok_src, ok_dst, pkv.PKV_SWAP_OUT)
+    hk64 = torch.zeros((L, NBH, Hkv, 2, B * 64), dtype=torch.bfloat16).pin_memory()
+    h64 = pkv.kv_pool_create(hk64, hk64.numel() * 2, L, NBH, Hkv, 64, B, pkv.PKV_BF16)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.swap_blocks_dma(dpool, h64, ok_src, ok_dst, pkv.PKV_SWAP_OUT)
+    torch.cuda.synchronize()
+    assert np.array_equal(_raw(hkv), before)
+    # a valid call after the refusals works
+    pkv.swap_blocks_dma(dpool, hpool, ok_src, ok_dst, pkv.PKV_SWAP_OUT)
+    torch.cuda.synchronize()
+    want = before.reshape(L, NBH, -1).copy()
+    _copy_host(want, _raw(dkv).reshape(L, NB, -1), [(3, 0), (7, 11)])
+    assert np.array_equal(_raw(hkv).reshape(L, NBH, -1), want)
+    for p in (dpool, hpool, ppool, h64):
+        p.destroy()
+
+
+@pytest.mark.parametrize("method", ["kernel", "dma"])
+def test_swaps_beside_a_decode(method):
+    """A swap out of two sequences' blocks and a swap in onto unused blocks run on one stream
+    while a decode of the whole batch runs on another: the decode's output equals the decode
+    run alone bit for bit, and both swaps land exactly."""
+    Hq, Hkv, D, B = 32, 8, 128, 16
+    lens = np.array([700, 1500, 333, 2048, 90, 1024], np.int32)
+    spec = workloads.Spec(0, "swap beside decode", len(lens), Hq, Hkv, D, "bf16", 2, seed=17)
+    t = workloads.make_tables(spec, lens=lens, seed=17)
+    b = workloads.make_batch(spec, device=DEV, tables=t, poison_unused=False)
+    L, NB = 2, t.num_blocks
+    victims = np.concatenate([t.block_tables[0, :44], t.block_tables[1, :94]]).astype(np.int32)
+    unused = np.flatnonzero(~t.used_blocks).astype(np.int32)[:20]
+    n = victims.shape[0]
+    hkv = torch.zeros((L, n + 20, Hkv, 2, B * D), dtype=torch.bfloat16).pin_memory()
+    g = torch.Generator().manual_seed(3)
+    hkv[:, n:] = workloads.randn(tuple(hkv[:, n:].shape), torch.bfloat16, g, "cpu")
+    dpool = pkv.kv_pool_create(b.kv_pool, b.kv_pool.numel() * 2, L, NB, Hkv, D, B, pkv.PKV_BF16)
+    hpool = pkv.kv_pool_create(hkv, hkv.numel() * 2, L, n + 20, Hkv, D, B, pkv.PKV_BF16)
+    alone = gpu_decode(b.q, b.k_pool[1], b.v_pool[1], b.block_tables, b.context_lens, spec.scale,
+                       Hq, Hkv, int(lens.max()))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()  # default priority
+    out = torch.full_like(b.q, 3.0)
+    ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(len(lens), Hq, Hkv, D, B,
+                                                               int(lens.max()), 0), DEV)
+    host_out = np.arange(n, dtype=np.int32)
+    host_in = np.arange(n, n + 20, dtype=np.int32)
+    say("swaps beside a decode:", method)
+    if method == "dma":
+        pkv.swap_blocks_dma(dpool, hpool, victims, host_out, pkv.PKV_SWAP_OUT, side)
+        pkv.swap_blocks_dma(dpool, hpool, host_in, unused, pkv.PKV_SWAP_IN, side)
+    else:
+        pkv.swap_blocks(dpool, hpool, _ids(victims, "device"), _ids(host_out, "device"),
+                        pkv.PKV_SWAP_OUT, side)
+        pkv.swap_blocks(dpool, hpool, _ids(host_in, "device"), _ids(unused, "device"),
+                        pkv.PKV_SWAP_IN, side)
+    pkv.paged_attention_decode(out, b.q, b.k_pool[1], b.v_pool[1], b.block_tables,
+                               b.context_lens, spec.scale, Hq, Hkv, D, B, int(lens.max()), 0, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), alone.view(torch.int16))
+    vic = torch.from_numpy(victims.astype(np.int64)).to(DEV)
+    assert torch.equal(hkv[:, :n].view(torch.int16), b.kv_pool[:, vic].cpu().view(torch.int16))
+    un = torch.from_numpy(unused.astype(np.int64)).to(DEV)
+    assert torch.equal(b.kv_pool[:, un].cpu().view(torch.int16), hkv[:, n:].view(torch.int16))
+    dpool.destroy()
+    hpool.destroy()
+
+
 def test_preempt_reuse_resume_decode():
     """The block manager preempts two of four sequences (one of them forked from another, so the
     group shares blocks), a new sequence takes and overwrites the freed device blocks, the group
