@@ -278,11 +278,23 @@ def test_swaps_beside_a_decode(method):
     hpool.destroy()
 
 
-def test_preempt_reuse_resume_decode():
+def _swap(method, dpool, hpool, pairs, direction):
+    """pairs[:, 0] -> pairs[:, 1] by the kernel (ids on the device) or the copy engines (ids on
+    the host)."""
+    src, dst = (np.ascontiguousarray(pairs[:, c], dtype=np.int32) for c in (0, 1))
+    if method == "dma":
+        pkv.swap_blocks_dma(dpool, hpool, src, dst, direction)
+    else:
+        pkv.swap_blocks(dpool, hpool, torch.from_numpy(src).to(DEV),
+                        torch.from_numpy(dst).to(DEV), direction)
+
+
+@pytest.mark.parametrize("method", ["kernel", "dma"])
+def test_preempt_reuse_resume_decode(method):
     """The block manager preempts two of four sequences (one of them forked from another, so the
     group shares blocks), a new sequence takes and overwrites the freed device blocks, the group
     is swapped back into different blocks, and decode of all four sequences equals the oracle on
-    the contents before the preemption."""
+    the contents before the preemption. Swaps by the kernel and by the copy engines."""
     Hq, Hkv, D, B, NB, NBH = 32, 8, 128, 16, 48, 32
     dt = torch.bfloat16
     bm = pkv.BlockManager(NB, B, num_host_blocks=NBH)
@@ -324,8 +336,7 @@ def test_preempt_reuse_resume_decode():
     say("preempt: swap out sequences 1 and 2")
     pairs = bm.swap_out([1, 2])
     assert pairs.shape[0] == 4                      # 1's 3 blocks (2 shared) + 2's private copy
-    pkv.swap_blocks(dpool, hpool, torch.from_numpy(pairs[:, 0].copy()).to(DEV),
-                    torch.from_numpy(pairs[:, 1].copy()).to(DEV), pkv.PKV_SWAP_OUT)
+    _swap(method, dpool, hpool, pairs, pkv.PKV_SWAP_OUT)
     torch.cuda.synchronize()
     freed = bm.num_free
     write_prompt(9, freed * B)                      # takes and overwrites every free block
@@ -333,8 +344,7 @@ def test_preempt_reuse_resume_decode():
     bm.release(9)                                   # its blocks return, holding its data
     say("resume: swap in sequences 2 and 1")
     pairs_in = bm.swap_in([2, 1])
-    pkv.swap_blocks(dpool, hpool, torch.from_numpy(pairs_in[:, 0].copy()).to(DEV),
-                    torch.from_numpy(pairs_in[:, 1].copy()).to(DEV), pkv.PKV_SWAP_IN)
+    _swap(method, dpool, hpool, pairs_in, pkv.PKV_SWAP_IN)
     bt1, cl1 = bm.tables(seqs, MB)
     assert cl1.tolist() == cl0.tolist()
     assert not np.array_equal(bt1[1:3], bt0[1:3])  # the group lives in other blocks now
