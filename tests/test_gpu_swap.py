@@ -250,22 +250,24 @@ def test_swaps_beside_a_decode(method):
     hpool = pkv.kv_pool_create(hkv, hkv.numel() * 2, L, n + 20, Hkv, D, B, pkv.PKV_BF16)
     alone = gpu_decode(b.q, b.k_pool[1], b.v_pool[1], b.block_tables, b.context_lens, spec.scale,
                        Hq, Hkv, int(lens.max()))
-    torch.cuda.synchronize()
-    side = torch.cuda.Stream()  # default priority
+    host_out = np.arange(n, dtype=np.int32)
+    host_in = np.arange(n, n + 20, dtype=np.int32)
+    # the kernel path reads its ids on the device: they are copied there (on this stream) before
+    # the side stream starts
+    dev_ids = [_ids(a, "device") for a in (victims, host_out, host_in, unused)]
     out = torch.full_like(b.q, 3.0)
     ws = pkv.new_workspace(pkv.paged_attention_workspace_bytes(len(lens), Hq, Hkv, D, B,
                                                                int(lens.max()), 0), DEV)
-    host_out = np.arange(n, dtype=np.int32)
-    host_in = np.arange(n, n + 20, dtype=np.int32)
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
     say("swaps beside a decode:", method)
     if method == "dma":
         pkv.swap_blocks_dma(dpool, hpool, victims, host_out, pkv.PKV_SWAP_OUT, side)
         pkv.swap_blocks_dma(dpool, hpool, host_in, unused, pkv.PKV_SWAP_IN, side)
     else:
-        pkv.swap_blocks(dpool, hpool, _ids(victims, "device"), _ids(host_out, "device"),
-                        pkv.PKV_SWAP_OUT, side)
-        pkv.swap_blocks(dpool, hpool, _ids(host_in, "device"), _ids(unused, "device"),
-                        pkv.PKV_SWAP_IN, side)
+        pkv.swap_blocks(dpool, hpool, dev_ids[0], dev_ids[1], pkv.PKV_SWAP_OUT, side)
+        pkv.swap_blocks(dpool, hpool, dev_ids[2], dev_ids[3], pkv.PKV_SWAP_IN, side)
     pkv.paged_attention_decode(out, b.q, b.k_pool[1], b.v_pool[1], b.block_tables,
                                b.context_lens, spec.scale, Hq, Hkv, D, B, int(lens.max()), 0, ws)
     torch.cuda.synchronize()
