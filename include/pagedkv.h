@@ -304,7 +304,10 @@ typedef enum { PKV_SWAP_OUT = 0, PKV_SWAP_IN = 1 } pkv_swap_dir;
  *                distinct and must not be sources.
  * One kernel reads or writes the host pool across the host link, ordered on `stream`: synchronize
  * the stream before reading swapped-out blocks on the host, and do not write the host blocks of a
- * swap-in while it is in flight. num_pairs in [0, 65535]; 0 is a no-op.
+ * swap-in while it is in flight. Ids in device memory are read by that kernel, so they must be
+ * written in stream order before it. A kernel that reaches into host memory starves work running
+ * beside it on other streams: a decode slows several-fold for as long as the swap lasts. For swaps
+ * that overlap a decode, use swap_blocks_dma. num_pairs in [0, 65535]; 0 is a no-op.
  * Errors: PKV_ERR_INVALID_ARG for null pools, mismatched geometry, a bad direction, or a host pool
  * or id array that is not device-visible (pinned host or device) memory, detected before any
  * launch.
