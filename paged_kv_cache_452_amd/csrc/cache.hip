@@ -113,13 +113,13 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
   }
 }
 
-// Whole-block copies between two pools of one geometry: the same device pool (copy-on-write),
-// or a device pool and a pinned host pool (swapping). For pair i and layer L, the region of block
-// src[i] of the source (the K and V tiles of all kv heads: block_bytes, contiguous) is copied to
-// block dst[i] of the destination. One thread moves 16 bytes; the grid is (16-byte chunks of a
-// region / 256, pairs, layers), so consecutive workgroups stream consecutive 4 KiB of one region.
-// A pair with an id outside its pool is skipped. Pure streaming copy. (Measured on device pools:
-// one workgroup per region with 8 loads in flight per thread was 15% slower.)
+// Whole-block copies within the device pool (copy-on-write; swapping to and from host memory uses
+// block_copy_link_kernel below). For pair i and layer L, the region of block src[i] (the K and V
+// tiles of all kv heads: block_bytes, contiguous) is copied to block dst[i]. One thread moves 16
+// bytes; the grid is (16-byte chunks of a region / 256, pairs, layers), so consecutive workgroups
+// stream consecutive 4 KiB of one region. A pair with an id outside its pool is skipped. Pure
+// streaming copy. (Measured on device pools: one workgroup per region with 8 loads in flight per
+// thread was 15% slower.)
 __global__ __launch_bounds__(256) void block_copy_kernel(BlockCopy c) {
   const size_t chunk = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (chunk * 16 >= c.block_bytes) return;
