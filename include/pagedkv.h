@@ -23,11 +23,13 @@
  *     A NULL stream is the HIP null stream.
  *   - Argument errors found on the host come back as a negative `pkv_status` and nothing is
  *     launched. A failed kernel launch returns PKV_ERR_HIP. Nothing is thrown across the ABI.
- *   - Device-resident indices (block table entries, context lengths, slots) are NOT validated:
- *     block ids must lie in [0, num_blocks), context lengths in [0, max_context_len] and
- *     [0, max_blocks_per_seq*block_size], and slots must be distinct within one call.
- *     Violations are undefined behaviour (out-of-bounds device accesses). On request,
- *     paged_attention_check_inputs counts them on the device (a debug aid).
+ *   - Device-resident indices (block table entries, slots) are NOT validated: the block ids a
+ *     sequence uses (the first ceil(n / block_size) of its row) must lie in [0, num_blocks), and
+ *     slots must be distinct within one call. Violations are undefined behaviour (out-of-bounds
+ *     device accesses). Context lengths are clamped to [0, max_blocks_per_seq*block_size] (a
+ *     negative length decodes as an empty sequence), but the clamped length must still name valid
+ *     blocks. max_context_len sizes the grid and workspace; lengths above it decode correctly.
+ *     On request, paged_attention_check_inputs counts violations on the device (a debug aid).
  *   - A call's output (out; the pool for the scatter calls) must not overlap its other inputs:
  *     the kernels read inputs while they write the output.
  *   - Stateless and thread-safe: concurrent calls are fine as long as their outputs do not alias.

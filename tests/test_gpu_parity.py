@@ -601,3 +601,26 @@ def test_planes_given_as_device_addresses():
     assert torch.equal(p1.view(torch.int16), p2.view(torch.int16))
     ref = oracle_decode(b.q, k, v, t.block_tables, lens, spec.scale, Hq, Hkv, t.num_blocks)
     assert_close(o2, ref, "planes as device addresses")
+
+
+def test_context_lengths_are_clamped_to_the_table_row():
+    """The decode clamps each context length to [0, max_blocks_per_seq * block_size]: a negative
+    length decodes like an empty sequence (zeros), and a length past the table row like the full
+    row (here a row of full blocks). max_context_len only sizes the grid: lengths above it still
+    decode to the oracle's result."""
+    spec, t, b = _random_case(16, 4, 128, [304, 80, 40], seed=29)
+    assert t.block_tables.shape[1] * 16 == 304          # sequence 0 fills its whole row
+    k, v = _layer(b)
+    given = torch.tensor([10000, 80, -7], dtype=torch.int32, device=DEV)
+    meant = np.array([304, 80, 0], np.int32)
+    say("clamped context lengths")
+    got = gpu_decode(b.q, k, v, b.block_tables, given, spec.scale, 16, 4, 304)
+    want = gpu_decode(b.q, k, v, b.block_tables, torch.from_numpy(meant).to(DEV), spec.scale, 16,
+                      4, 304)
+    small_hint = gpu_decode(b.q, k, v, b.block_tables, given, spec.scale, 16, 4, 16)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    assert not got[2].float().abs().any()
+    ref = oracle_decode(b.q, k, v, t.block_tables, meant, spec.scale, 16, 4, t.num_blocks)
+    assert_close(got, ref, "clamped lengths")
+    assert_close(small_hint, ref, "lengths above max_context_len")
