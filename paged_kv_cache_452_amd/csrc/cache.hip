@@ -5,7 +5,8 @@
 // kernel writes the token's K and V rows for every kv head into that slot of the pool's tiles.
 // One thread moves eight consecutive dims (16 bytes) of one (token, kv head): the K tile keeps
 // those eight dims contiguous, so K is one 16-byte store; the V tile keeps four consecutive
-// tokens of one dim together, so V is eight 2-byte stores.
+// tokens of one dim together, so V is eight 2-byte stores. A wavefront takes consecutive tokens
+// of one kv head, so the stores of a prompt's consecutive tokens land side by side and merge.
 
 #include "pkv_internal.h"
 #include "pkv_link.h"
@@ -16,6 +17,21 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// Tokens per wavefront of the scatter kernels: 64 lanes over a token's D / 8 chunks of 16 bytes.
+// Consecutive tokens of one wavefront that fill consecutive slots (a prompt's do) then write
+// adjacent bytes in one store instruction, which the memory pipeline merges: their K chunks are
+// 16 bytes apart and their V values 2 bytes apart (1 byte in fp8 pools).
+template <int D>
+constexpr int scatter_tokens() {
+  return 64 / (D / 8);
+}
+
+// Threads of a scatter launch: whole wavefronts of scatter_tokens<D>() tokens per kv head.
+template <int D>
+long scatter_threads(int num_tokens, int num_kv_heads) {
+  return (long)((num_tokens + scatter_tokens<D>() - 1) / scatter_tokens<D>()) * num_kv_heads * 64;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const unsigned short* __restrict__ key, const unsigned short* __restrict__ value,
@@ -24,12 +40,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     int64_t num_slots) {
   constexpr int kChunks = D / 8;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long total = (long)num_tokens * num_kv_heads * kChunks;
-  if (gid >= total) return;
+  // a wavefront: one kv head, scatter_tokens<D>() consecutive tokens, each token's 16-byte chunks
+  // on consecutive lanes
   const int c = (int)(gid % kChunks);
-  const long r = gid / kChunks;
-  const int h = (int)(r % num_kv_heads);
-  const long i = r / num_kv_heads;
+  const long i = (gid / 64 / num_kv_heads) * scatter_tokens<D>() + (gid % 64) / kChunks;
+  const int h = (int)(gid / 64 % num_kv_heads);
+  if (i >= num_tokens) return;
   const int64_t slot = slot_mapping[i];
   if (slot < 0 || slot >= num_slots) return;  // skipped: negative or past the pool
   const int64_t b = slot / block_size;
@@ -67,12 +83,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     int64_t num_slots, float k_inv, float v_inv) {
   constexpr int kChunks = D / 8;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long total = (long)num_tokens * num_kv_heads * kChunks;
-  if (gid >= total) return;
+  // a wavefront: one kv head, scatter_tokens<D>() consecutive tokens, each token's 16-byte chunks
+  // on consecutive lanes
   const int c = (int)(gid % kChunks);
-  const long r = gid / kChunks;
-  const int h = (int)(r % num_kv_heads);
-  const long i = r / num_kv_heads;
+  const long i = (gid / 64 / num_kv_heads) * scatter_tokens<D>() + (gid % 64) / kChunks;
+  const int h = (int)(gid / 64 % num_kv_heads);
+  if (i >= num_tokens) return;
   const int64_t slot = slot_mapping[i];
   if (slot < 0 || slot >= num_slots) return;  // skipped: negative or past the pool
   const int64_t b = slot / block_size;
@@ -208,8 +224,9 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         int num_blocks, bool src_bf16, float k_inv_scale,
                                         float v_inv_scale, hipStream_t stream) {
   const int64_t num_slots = (int64_t)num_blocks * block_size;
-  const long total = (long)num_tokens * num_kv_heads * (head_dim / 8);
-  if (total == 0) return hipSuccess;
+  if (num_tokens == 0 || num_kv_heads == 0) return hipSuccess;
+  const long total = head_dim == 128 ? scatter_threads<128>(num_tokens, num_kv_heads)
+                                     : scatter_threads<64>(num_tokens, num_kv_heads);
   const unsigned blocks = (unsigned)((total + 255) / 256);
   const auto* k = (const unsigned short*)key;
   const auto* v = (const unsigned short*)value;
@@ -233,8 +250,9 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     int head_dim, int block_size, int num_blocks,
                                     hipStream_t stream) {
   const int64_t num_slots = (int64_t)num_blocks * block_size;
-  const long total = (long)num_tokens * num_kv_heads * (head_dim / 8);
-  if (total == 0) return hipSuccess;
+  if (num_tokens == 0 || num_kv_heads == 0) return hipSuccess;
+  const long total = head_dim == 128 ? scatter_threads<128>(num_tokens, num_kv_heads)
+                                     : scatter_threads<64>(num_tokens, num_kv_heads);
   const unsigned blocks = (unsigned)((total + 255) / 256);
   const auto* k = (const unsigned short*)key;
   const auto* v = (const unsigned short*)value;

@@ -202,3 +202,68 @@ def test_random_multi_token_scatter_bit_exact(seed, fp8):
         torch.cuda.synchronize()
         assert np.array_equal(words(k), kw), "K pool differs"
         assert np.array_equal(words(v), vw), "V pool differs"
+
+
+def _prompt_case(seed):
+    """A scatter in prompt order: several sequences' prompts, each a run of consecutive slots
+    through its blocks starting at a random offset (mid-group too); two of them interleaved token
+    by token (so their 4-slot groups are not whole in call order); a skipped and a past-the-pool
+    entry dropped into one run."""
+    rng = np.random.default_rng(6000 + seed)
+    Hkv = int(rng.choice([1, 2, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.choice([16, 32]))
+    dtype = torch.bfloat16 if rng.random() < 0.5 else torch.float16
+    NB = int(rng.integers(24, 80))
+    order = iter(rng.permutation(NB).tolist())
+    runs = []
+    for _ in range(int(rng.integers(3, 6))):
+        start = int(rng.integers(0, B))           # the prompt continues a partly filled block
+        n = int(rng.integers(1, 3 * B))
+        blocks = [next(order) for _ in range(-(-(start + n) // B))]
+        runs.append([blocks[(start + p) // B] * B + (start + p) % B for p in range(n)])
+    a, b = runs.pop(), runs.pop()
+    mixed = [x for pair in zip(a, b) for x in pair] + a[len(b):] + b[len(a):]
+    runs.append(mixed)
+    where = int(rng.integers(0, len(runs[0]) + 1))
+    runs[0][where:where] = [-1, NB * B + 2]
+    slots = np.array([x for r in runs for x in r], np.int64)
+    return Hkv, D, B, dtype, NB, slots
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prompt_order_scatter_bit_exact(seed, fp8):
+    """reshape_and_cache of prompts in order, where consecutive tokens fill whole 4-slot groups
+    of the V tile and are written a group at a time: the whole pool equals the oracle's token by
+    token scatter."""
+    Hkv, D, B, dtype, NB, slots = _prompt_case(seed)
+    T = len(slots)
+    skipped = np.where(slots >= NB * B, -1, slots)  # the oracle takes a skipped slot as -1
+    gen = torch.Generator(device=DEV).manual_seed(seed + 100)
+    key = workloads.randn((T, Hkv, D), dtype, gen, DEV)
+    value = workloads.randn((T, Hkv, D), dtype, gen, DEV)
+    sm = torch.from_numpy(slots).to(DEV)
+    say("prompt-order scatter", seed, "fp8" if fp8 else str(dtype), f"Hkv={Hkv} D={D} B={B} T={T}")
+    if fp8:
+        pool = workloads.new_pool(1, NB, Hkv, B, D, torch.uint8, DEV)
+        pool.copy_(torch.randint(0, 256, pool.shape, generator=gen, device=DEV, dtype=torch.uint8))
+        k, v = (p[0] for p in workloads.planes(pool))
+        kb, vb = codes(k), codes(v)
+        oracle.reshape_and_cache8(kb, vb, key.cpu(), value.cpu(), oracle.BF16 if dtype ==
+                                  torch.bfloat16 else oracle.FP16, 0.25, 0.5, skipped, Hkv, D, B,
+                                  NB)
+        pkv.reshape_and_cache_fp8(key, value, k, v, sm, NB, 0.25, 0.5, B)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes(k), kb), "K pool differs"
+        assert np.array_equal(codes(v), vb), "V pool differs"
+    else:
+        pool = workloads.new_pool(1, NB, Hkv, B, D, dtype, DEV)
+        pool.copy_(workloads.randn(pool.shape, dtype, gen, DEV))
+        k, v = (p[0] for p in workloads.planes(pool))
+        kw, vw = words(k), words(v)
+        oracle.reshape_and_cache(kw, vw, key.cpu(), value.cpu(), skipped, Hkv, D, B, NB)
+        pkv.reshape_and_cache(key, value, k, v, sm, NB, B)
+        torch.cuda.synchronize()
+        assert np.array_equal(words(k), kw), "K pool differs"
+        assert np.array_equal(words(v), vw), "V pool differs"
