@@ -340,7 +340,6 @@ pkv_status swap_blocks_dma(const pkv_pool* device_pool, const pkv_pool* host_poo
                            pkv_swap_dir direction, hipStream_t stream);
 
 /*
- * Host block manager: the bookkeeping of which physical blocks hold which sequence's tokens/*
  * Host block manager: the bookkeeping of which physical blocks hold which sequence's tokens
  * ("PagedAttention and KV Cache Management" (blog.sejan.dev), sections "How Block Paging Operates
  * During Generation" (on-demand and boundary allocation), "Advanced Memory Sharing: Prefix Caching

@@ -1,6 +1,7 @@
 /* The library's ABI used from plain C (compiled as C11 by gcc, linked against libpagedkv.so):
  * the header must be valid C, and the host-side entry points behave as the header states. Only
- * calls that touch no GPU: pool sizing, status strings and the host block manager. */
+ * calls that touch no GPU: pool sizing, status strings, the host block manager, and the argument
+ * refusals of swap_blocks_dma. */
 #include "pagedkv.h"
 
 #include <stdio.h>
@@ -67,5 +68,21 @@ int main(void) {
   kv_block_manager_destroy(bm);
   kv_block_manager_destroy(NULL);
   printf("C ABI checks: failures %d\n", failures);
+  /* swap_blocks_dma: its argument refusals come before any HIP call (pools here describe a host
+   * arena; nothing is copied). */
+  static unsigned char arena[4096] __attribute__((aligned(256)));
+  pkv_pool* pa = NULL;
+  pkv_pool* pb = NULL;
+  CHECK(kv_pool_create(&pa, arena, sizeof arena, 1, 1, 1, 64, 16, PKV_FP8_E4M3) == PKV_OK);
+  CHECK(kv_pool_create(&pb, arena, sizeof arena, 1, 1, 1, 128, 16, PKV_FP8_E4M3) == PKV_OK);
+  int32_t one[1] = {0};
+  CHECK(swap_blocks_dma(NULL, pa, one, one, 1, PKV_SWAP_OUT, NULL) == PKV_ERR_INVALID_ARG);
+  CHECK(swap_blocks_dma(pa, pa, one, one, 1, (pkv_swap_dir)7, NULL) == PKV_ERR_INVALID_ARG);
+  CHECK(swap_blocks_dma(pa, pb, one, one, 1, PKV_SWAP_OUT, NULL) == PKV_ERR_INVALID_ARG);
+  CHECK(swap_blocks_dma(pa, pa, one, one, -1, PKV_SWAP_OUT, NULL) == PKV_ERR_INVALID_ARG);
+  CHECK(swap_blocks_dma(pa, pa, NULL, NULL, 0, PKV_SWAP_IN, NULL) == PKV_OK); /* no-op */
+  kv_pool_destroy(pa);
+  kv_pool_destroy(pb);
+
   return failures != 0;
 }
